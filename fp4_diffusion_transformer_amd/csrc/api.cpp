@@ -1,0 +1,155 @@
+// C ABI of libfp4dit.so (declared in include/fp4dit.h): host-side argument
+// validation, then the launch on the caller's stream.  Validation never
+// dereferences a pointer and runs before any HIP call, so a non-OK status
+// other than FP4DIT_E_LAUNCH means nothing was enqueued.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/fp4dit.h"
+#include "launch.hpp"
+
+namespace {
+
+using fp4dit::kGemmKMultiple;
+using fp4dit::kGemmNMultiple;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool valid_dtype(fp4dit_dtype d) { return d == FP4DIT_F32 || d == FP4DIT_BF16; }
+fp4dit_status launched(hipError_t e) { return e == hipSuccess ? FP4DIT_OK : FP4DIT_E_LAUNCH; }
+
+// Byte offsets inside the GEMM operands are 32-bit.
+constexpr int64_t kMaxOperandBytes = (int64_t(1) << 31) - 1;
+
+fp4dit_status check_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                         const uint8_t* bc, const uint8_t* bs) {
+    if (M < 0 || N <= 0 || K <= 0) return FP4DIT_E_SHAPE;
+    if (N % kGemmNMultiple != 0 || K % kGemmKMultiple != 0) return FP4DIT_E_SHAPE;
+    if (M * (K / 2) > kMaxOperandBytes || N * (K / 2) > kMaxOperandBytes) return FP4DIT_E_SHAPE;
+    if (M == 0) return FP4DIT_OK;
+    if (!ac || !as || !bc || !bs) return FP4DIT_E_NULL;
+    if (!aligned(ac, 16) || !aligned(bc, 16) || !aligned(as, 4) || !aligned(bs, 4)) return FP4DIT_E_ALIGN;
+    return FP4DIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp4dit_status_string(fp4dit_status s) {
+    switch (s) {
+        case FP4DIT_OK: return "ok";
+        case FP4DIT_E_NULL: return "null pointer";
+        case FP4DIT_E_SHAPE: return "invalid shape";
+        case FP4DIT_E_ALIGN: return "misaligned pointer";
+        case FP4DIT_E_UNSUPPORTED: return "unsupported argument";
+        case FP4DIT_E_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+int32_t fp4dit_swiglu_interleave_group(void) { return fp4dit::kSwigluGroup; }
+
+fp4dit_status fp4dit_quantize_mxfp4(const void* x, fp4dit_dtype x_dtype, int64_t rows, int64_t cols,
+                                    uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+    if (!valid_dtype(x_dtype)) return FP4DIT_E_UNSUPPORTED;
+    if (rows < 0 || cols < 0 || cols % 32 != 0) return FP4DIT_E_SHAPE;
+    if (rows == 0 || cols == 0) return FP4DIT_OK;
+    if (rows * (cols / 32) > (int64_t(1) << 36)) return FP4DIT_E_SHAPE;
+    if (!x || !codes || !scales) return FP4DIT_E_NULL;
+    if (!aligned(x, 16) || !aligned(codes, 16)) return FP4DIT_E_ALIGN;
+    return launched(fp4dit::launch_quantize(x, x_dtype == FP4DIT_BF16, rows, cols, codes, scales, stream));
+}
+
+fp4dit_status fp4dit_block_transform(const void* x, fp4dit_dtype x_dtype, int64_t rows, int64_t cols,
+                                     const uint16_t* t_bf16, int64_t n_t, void* y, fp4dit_dtype y_dtype,
+                                     uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+    if (!valid_dtype(x_dtype) || (y && !valid_dtype(y_dtype))) return FP4DIT_E_UNSUPPORTED;
+    if ((codes == nullptr) != (scales == nullptr)) return FP4DIT_E_UNSUPPORTED;
+    if (rows < 0 || cols < 0 || cols % 32 != 0) return FP4DIT_E_SHAPE;
+    if (n_t != 1 && n_t != cols / 32) return FP4DIT_E_SHAPE;
+    if (rows == 0 || cols == 0) return FP4DIT_OK;
+    if (cols / 32 > (int64_t(1) << 20) || rows > (int64_t(1) << 23)) return FP4DIT_E_SHAPE;  // grid.y <= 65535
+    if (!x || !t_bf16) return FP4DIT_E_NULL;
+    if (!y && !codes) return FP4DIT_E_NULL;
+    if (!aligned(x, 16) || !aligned(t_bf16, 2) || (y && !aligned(y, 16)) || (codes && !aligned(codes, 16)))
+        return FP4DIT_E_ALIGN;
+    return launched(fp4dit::launch_block_transform(x, x_dtype == FP4DIT_BF16, rows, cols, t_bf16, n_t, y,
+                                                   y_dtype == FP4DIT_BF16, codes, scales, stream));
+}
+
+fp4dit_status fp4dit_fold_inverse_transform(const float* w, int64_t K, int64_t N, const uint16_t* t_bf16,
+                                            int64_t n_t, float* w_out, hipStream_t stream) {
+    if (K < 0 || N < 0 || K % 32 != 0) return FP4DIT_E_SHAPE;
+    if (n_t != 1 && n_t != K / 32) return FP4DIT_E_SHAPE;
+    if (K == 0 || N == 0) return FP4DIT_OK;
+    if (K / 32 > 65535) return FP4DIT_E_SHAPE;
+    if (!w || !t_bf16 || !w_out) return FP4DIT_E_NULL;
+    if (w == w_out) return FP4DIT_E_UNSUPPORTED;
+    if (!aligned(w, 4) || !aligned(w_out, 4) || !aligned(t_bf16, 2)) return FP4DIT_E_ALIGN;
+    return launched(fp4dit::launch_fold_inverse(w, K, N, t_bf16, n_t, w_out, stream));
+}
+
+fp4dit_status fp4dit_pack_weight(const void* w, fp4dit_dtype w_dtype, int64_t K, int64_t N,
+                                 int32_t interleave_group, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t stream) {
+    if (!valid_dtype(w_dtype)) return FP4DIT_E_UNSUPPORTED;
+    if (interleave_group < 0) return FP4DIT_E_UNSUPPORTED;
+    if (K < 0 || N < 0 || K % 32 != 0) return FP4DIT_E_SHAPE;
+    if (interleave_group > 0 && N % (2 * (int64_t)interleave_group) != 0) return FP4DIT_E_SHAPE;
+    if (K == 0 || N == 0) return FP4DIT_OK;
+    if (K / 32 > 65535) return FP4DIT_E_SHAPE;
+    if (!w || !codes || !scales) return FP4DIT_E_NULL;
+    if (!aligned(codes, 16) || !aligned(w, w_dtype == FP4DIT_BF16 ? 2 : 4)) return FP4DIT_E_ALIGN;
+    return launched(fp4dit::launch_pack_weight(w, w_dtype == FP4DIT_BF16, K, N, interleave_group, codes,
+                                               scales, stream));
+}
+
+fp4dit_status fp4dit_gemm_fp4_epilogue_none(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                                            const uint8_t* a_scales, const uint8_t* b_codes,
+                                            const uint8_t* b_scales, void* out, fp4dit_dtype out_dtype,
+                                            hipStream_t stream) {
+    if (!valid_dtype(out_dtype)) return FP4DIT_E_UNSUPPORTED;
+    const fp4dit_status st = check_gemm(M, N, K, a_codes, a_scales, b_codes, b_scales);
+    if (st != FP4DIT_OK || M == 0) return st;
+    if (!out) return FP4DIT_E_NULL;
+    if (!aligned(out, 16)) return FP4DIT_E_ALIGN;
+    return launched(fp4dit::launch_gemm_none(M, N, K, a_codes, a_scales, b_codes, b_scales, out,
+                                             out_dtype == FP4DIT_BF16, stream));
+}
+
+fp4dit_status fp4dit_gemm_fp4_epilogue_rmsnorm_head(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                                                    const uint8_t* a_scales, const uint8_t* b_codes,
+                                                    const uint8_t* b_scales, int32_t head_dim,
+                                                    int64_t n_norm_cols, const float* norm_w, float eps,
+                                                    void* out, fp4dit_dtype out_dtype, hipStream_t stream) {
+    if (!valid_dtype(out_dtype)) return FP4DIT_E_UNSUPPORTED;
+    if (head_dim != 128 && head_dim != 256) return FP4DIT_E_UNSUPPORTED;
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return FP4DIT_E_UNSUPPORTED;
+    const fp4dit_status st = check_gemm(M, N, K, a_codes, a_scales, b_codes, b_scales);
+    if (st != FP4DIT_OK) return st;
+    if (n_norm_cols < 0 || n_norm_cols > N || n_norm_cols % head_dim != 0) return FP4DIT_E_SHAPE;
+    if (M == 0) return FP4DIT_OK;
+    if (!out || (n_norm_cols > 0 && !norm_w)) return FP4DIT_E_NULL;
+    if (!aligned(out, 16) || (n_norm_cols > 0 && !aligned(norm_w, 16))) return FP4DIT_E_ALIGN;
+    return launched(fp4dit::launch_gemm_rmsnorm(M, N, K, a_codes, a_scales, b_codes, b_scales, head_dim,
+                                                n_norm_cols, norm_w, eps, out, out_dtype == FP4DIT_BF16,
+                                                stream));
+}
+
+fp4dit_status fp4dit_gemm_fp4_epilogue_swiglu(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                                              const uint8_t* a_scales, const uint8_t* b_codes,
+                                              const uint8_t* b_scales, void* out, fp4dit_dtype out_dtype,
+                                              uint8_t* out_codes, uint8_t* out_scales, hipStream_t stream) {
+    if (out && !valid_dtype(out_dtype)) return FP4DIT_E_UNSUPPORTED;
+    if ((out_codes == nullptr) != (out_scales == nullptr)) return FP4DIT_E_UNSUPPORTED;
+    const fp4dit_status st = check_gemm(M, N, K, a_codes, a_scales, b_codes, b_scales);
+    if (st != FP4DIT_OK) return st;
+    if (N % (2 * fp4dit::kSwigluGroup) != 0) return FP4DIT_E_SHAPE;
+    if (M == 0) return FP4DIT_OK;
+    if (!out && !out_codes) return FP4DIT_E_NULL;
+    if ((out && !aligned(out, 16)) || (out_codes && !aligned(out_codes, 16))) return FP4DIT_E_ALIGN;
+    return launched(fp4dit::launch_gemm_swiglu(M, N, K, a_codes, a_scales, b_codes, b_scales, out,
+                                               out_dtype == FP4DIT_BF16, out_codes, out_scales, stream));
+}
+
+}  // extern "C"

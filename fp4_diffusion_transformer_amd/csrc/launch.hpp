@@ -1,0 +1,44 @@
+// Internal launchers of the fp4dit kernels, called by the C ABI layer after
+// argument validation.  Each enqueues on `stream` and returns
+// hipGetLastError() of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4dit {
+
+hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols,
+                           uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+hipError_t launch_pack_weight(const void* w, bool bf16, int64_t K, int64_t N, int group,
+                              uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+hipError_t launch_block_transform(const void* x, bool x_bf16, int64_t rows, int64_t cols,
+                                  const uint16_t* t, int64_t n_t, void* y, bool y_bf16,
+                                  uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+hipError_t launch_fold_inverse(const float* w, int64_t K, int64_t N, const uint16_t* t, int64_t n_t,
+                               float* w_out, hipStream_t stream);
+
+hipError_t launch_gemm_none(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                            const uint8_t* bc, const uint8_t* bs, void* out, bool out_bf16,
+                            hipStream_t stream);
+
+hipError_t launch_gemm_rmsnorm(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                               const uint8_t* bc, const uint8_t* bs, int head_dim, int64_t n_norm,
+                               const float* norm_w, float eps, void* out, bool out_bf16,
+                               hipStream_t stream);
+
+hipError_t launch_gemm_swiglu(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                              const uint8_t* bc, const uint8_t* bs, void* out, bool out_bf16,
+                              uint8_t* out_codes, uint8_t* out_scales, hipStream_t stream);
+
+// Interleave group of the SwiGLU epilogue: channel blocks of 32 alternate
+// gate / up, matching one 32x32 MFMA output block per half.
+constexpr int kSwigluGroup = 32;
+// GEMM tiling constraints checked by the ABI layer.
+constexpr int64_t kGemmNMultiple = 256;
+constexpr int64_t kGemmKMultiple = 256;
+
+}  // namespace fp4dit

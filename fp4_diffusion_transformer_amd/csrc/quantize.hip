@@ -1,0 +1,121 @@
+// MXFP4 quantisation kernels: online activation quantisation and offline
+// weight packing (transpose to [N][K], optional SwiGLU column interleave).
+//
+// fal, "Running the transformer in FP4" (e2m1 elements) and the QAD section
+// (weights quantised statically for inference); KroQuant, "Deep analysis"
+// (MXFP4: 32-element blocks with a shared power-of-two scale); fal, "Fusing
+// gated SiLU" (gate/up columns permuted once at packing time).
+//
+// Activation quantisation is HBM-bound: 2 (bf16) or 4 (fp32) bytes in and
+// 17/32 byte out per element.  Four lanes share a 32-element block; each
+// lane loads 8 consecutive elements (16 B of bf16), so a wave reads 1 KiB of
+// contiguous memory per load and writes 256 contiguous bytes of codes.  The
+// block amax is reduced over the four lanes with DPP quad permutes.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace fp4dit {
+
+template <bool kBf16>
+__global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ x,
+                                                       uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales,
+                                                       int64_t nblocks) {
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t blk = gid >> 2;
+    const int part = (int)(gid & 3);
+    if (blk >= nblocks) return;                  // whole quads leave together
+    uint32_t xb[8];
+    const int64_t elem = blk * 32 + part * 8;
+    if (kBf16) {
+        const v4u v = *reinterpret_cast<const v4u*>(static_cast<const uint16_t*>(x) + elem);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            xb[2 * i] = v[i] << 16;
+            xb[2 * i + 1] = v[i] & 0xFFFF0000u;
+        }
+    } else {
+        const v4u* p = reinterpret_cast<const v4u*>(static_cast<const float*>(x) + elem);
+        const v4u v0 = p[0], v1 = p[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            xb[i] = v0[i];
+            xb[4 + i] = v1[i];
+        }
+    }
+    uint32_t amax = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t a = xb[i] & 0x7FFFFFFFu;
+        amax = a > amax ? a : amax;
+    }
+    amax = max_quad_u(amax);
+    const uint32_t sc = e8m0_from_amax_bits(amax);
+    const uint32_t w = sc == 0xFFu ? 0u : e2m1_pack8(xb, sc);
+    reinterpret_cast<uint32_t*>(codes)[blk * 4 + part] = w;
+    if (part == 0) scales[blk] = (uint8_t)sc;
+}
+
+// One thread per output block (physical column p, K-block kb): gathers the 32
+// weights of logical column src(p), rows 32kb..32kb+31, and encodes them.
+template <bool kBf16>
+__global__ __launch_bounds__(256) void pack_weight_kernel(const void* __restrict__ w,
+                                                          int64_t K, int64_t N, int group,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t kb = blockIdx.y;
+    if (p >= N) return;
+    int64_t src = p;
+    if (group > 0) {
+        const int64_t j = (p / (2 * group)) * group + p % group;
+        src = ((p / group) & 1) ? (N / 2 + j) : j;
+    }
+    uint32_t xb[32];
+    uint32_t amax = 0u;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+        const int64_t idx = (kb * 32 + r) * N + src;
+        uint32_t b;
+        if (kBf16) {
+            b = (uint32_t)static_cast<const uint16_t*>(w)[idx] << 16;
+        } else {
+            b = __float_as_uint(static_cast<const float*>(w)[idx]);
+        }
+        xb[r] = b;
+        const uint32_t a = b & 0x7FFFFFFFu;
+        amax = a > amax ? a : amax;
+    }
+    const uint32_t sc = e8m0_from_amax_bits(amax);
+    v4u out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = sc == 0xFFu ? 0u : e2m1_pack8(xb + 8 * i, sc);
+    *reinterpret_cast<v4u*>(codes + p * (K / 2) + kb * 16) = out;
+    scales[p * (K / 32) + kb] = (uint8_t)sc;
+}
+
+hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols,
+                           uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+    const int64_t nblocks = rows * (cols / 32);
+    const int64_t threads = nblocks * 4;
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    if (bf16) {
+        hipLaunchKernelGGL(quantize_kernel<true>, grid, dim3(256), 0, stream, x, codes, scales, nblocks);
+    } else {
+        hipLaunchKernelGGL(quantize_kernel<false>, grid, dim3(256), 0, stream, x, codes, scales, nblocks);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_weight(const void* w, bool bf16, int64_t K, int64_t N, int group,
+                              uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+    const dim3 grid((unsigned)((N + 255) / 256), (unsigned)(K / 32));
+    if (bf16) {
+        hipLaunchKernelGGL(pack_weight_kernel<true>, grid, dim3(256), 0, stream, w, K, N, group, codes, scales);
+    } else {
+        hipLaunchKernelGGL(pack_weight_kernel<false>, grid, dim3(256), 0, stream, w, K, N, group, codes, scales);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace fp4dit

@@ -1,0 +1,237 @@
+// Block-local activation transform (optionally fused with MXFP4 quantise)
+// and its offline weight-side inverse.
+//
+// KroQuant, "Background and overview": an invertible linear transform
+// smooths the activations and its inverse goes to the weights; it runs online
+// every denoising step, so its cost matters.  "Deep analysis": the
+// activations are split into independent 32-element blocks with one learned
+// matrix each, which turns the transform into small-tile matrix-core GEMMs.
+//
+// Online kernel (HBM-bound): one wave owns 32 tokens x 4 consecutive blocks
+// (128 channels, so each token row is read as 256 contiguous bytes).  Per
+// block it runs two bf16 MFMAs V_MFMA_F32_32X32X16_BF16 computing
+// Y_b^T = T_b^T . X_b^T, i.e. lane l ends with token l%32 and output
+// features 8a + 4(l/32) + r (a, r = 0..3) -- the same accumulator layout as
+// the GEMM epilogue, so the fused MXFP4 encoding is shared with it: the
+// block amax is one in-lane max plus one lane-swap (v_permlane32_swap).
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace fp4dit {
+namespace {
+
+typedef short v8s __attribute__((ext_vector_type(8)));
+
+// Encode one 32-wide block of an MFMA 32x32 accumulator row (this lane's 16
+// values hv[4a + r] = feature 8a + 4h + r) to MXFP4 and store it.
+__device__ __forceinline__ void store_mx_block(const float* hv, int lane, bool live,
+                                               uint8_t* codes16, uint8_t* scale1) {
+    const int h = lane >> 5;
+    uint32_t hb[16];
+    uint32_t amax = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        hb[i] = __float_as_uint(hv[i]);
+        const uint32_t a = hb[i] & 0x7FFFFFFFu;
+        amax = a > amax ? a : amax;
+    }
+    amax = max_xor32_u(amax);
+    const uint32_t sc = e8m0_from_amax_bits(amax);
+    uint32_t c16[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        uint32_t w = 0u;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w |= e2m1_code(hb[4 * a + r], sc) << (4 * r);
+        c16[a] = sc == 0xFFu ? 0u : w;
+    }
+    const uint32_t send = h == 0 ? (c16[2] | (c16[3] << 16)) : (c16[0] | (c16[1] << 16));
+    const uint32_t recv = partner_xor32(send, lane);
+    v2u st;
+    if (h == 0) {
+        st[0] = c16[0] | ((recv & 0xFFFFu) << 16);
+        st[1] = c16[1] | ((recv >> 16) << 16);
+    } else {
+        st[0] = (recv & 0xFFFFu) | (c16[2] << 16);
+        st[1] = (recv >> 16) | (c16[3] << 16);
+    }
+    if (live) {
+        *reinterpret_cast<v2u*>(codes16 + h * 8) = st;
+        if (h == 0) *scale1 = (uint8_t)sc;
+    }
+}
+
+constexpr int kTokIters = 4;           // 32-token groups per wave
+
+template <bool kXBf16, bool kYBf16>
+__global__ __launch_bounds__(256) void block_transform_kernel(const void* __restrict__ x, int64_t rows,
+                                                              int64_t cols, const uint16_t* __restrict__ t,
+                                                              int64_t n_t, void* __restrict__ y,
+                                                              uint8_t* __restrict__ codes,
+                                                              uint8_t* __restrict__ scales) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int h = lane >> 5;
+    const int r32 = lane & 31;
+    const int64_t nblk = cols / 32;
+    const int64_t b0 = ((int64_t)blockIdx.x * 4 + wave) * 4;   // first of this wave's 4 blocks
+    if (b0 >= nblk) return;                                     // wave-uniform
+    const int64_t tok_base = (int64_t)blockIdx.y * (32 * kTokIters);
+
+    // A operand: lane holds T_b^T row r32 (= column r32 of T_b) at
+    // k = 8h..8h+7 (first MFMA) and 16 + 8h.. (second MFMA).
+    v8s tf[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t b = b0 + j < nblk ? b0 + j : nblk - 1;
+        const uint16_t* tb = t + (n_t == 1 ? 0 : b) * 1024;
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tf[j][half][e] = (short)tb[(16 * half + 8 * h + e) * 32 + r32];
+    }
+
+    for (int it = 0; it < kTokIters; ++it) {
+        const int64_t tok = tok_base + it * 32 + r32;
+        const bool live = tok < rows;
+        const int64_t trow = live ? tok : rows - 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t b = b0 + j;
+            if (b >= nblk) break;                                   // wave-uniform
+            v8s xf[2];
+            const int64_t e0 = trow * cols + b * 32;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int64_t e = e0 + 16 * half + 8 * h;
+                if (kXBf16) {
+                    const v4u v = *reinterpret_cast<const v4u*>(static_cast<const uint16_t*>(x) + e);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        xf[half][2 * i] = (short)(v[i] & 0xFFFFu);
+                        xf[half][2 * i + 1] = (short)(v[i] >> 16);
+                    }
+                } else {
+                    const v4f* p = reinterpret_cast<const v4f*>(static_cast<const float*>(x) + e);
+                    const v4f v0 = p[0], v1 = p[1];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        xf[half][i] = (short)f32_to_bf16_bits(v0[i]);
+                        xf[half][4 + i] = (short)f32_to_bf16_bits(v1[i]);
+                    }
+                }
+            }
+            v16f acc = {};
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[j][0], xf[0], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[j][1], xf[1], acc, 0, 0, 0);
+            float hv[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) hv[i] = acc[i];
+            if (y != nullptr && live) {
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int64_t o = tok * cols + b * 32 + 8 * a + 4 * h;
+                    if (kYBf16) {
+                        v2u v;
+                        v[0] = pack_bf16x2(hv[4 * a], hv[4 * a + 1]);
+                        v[1] = pack_bf16x2(hv[4 * a + 2], hv[4 * a + 3]);
+                        *reinterpret_cast<v2u*>(static_cast<uint16_t*>(y) + o) = v;
+                    } else {
+                        *reinterpret_cast<v4f*>(static_cast<float*>(y) + o) =
+                            (v4f){hv[4 * a], hv[4 * a + 1], hv[4 * a + 2], hv[4 * a + 3]};
+                    }
+                }
+            }
+            if (codes != nullptr) {
+                store_mx_block(hv, lane, live, codes + tok * (cols / 2) + b * 16, scales + tok * nblk + b);
+            }
+        }
+    }
+}
+
+// W'_b = T_b^-1 . W_b.  One workgroup per (block b, 256 columns): the
+// workgroup LU-factorises T_b in fp64 with partial pivoting in LDS, then every thread
+// solves for one column (forward then back substitution) and stores fp32.
+__global__ __launch_bounds__(256) void fold_inverse_kernel(const float* __restrict__ w, int64_t K, int64_t N,
+                                                           const uint16_t* __restrict__ t, int64_t n_t,
+                                                           float* __restrict__ w_out) {
+    __shared__ double lu[32][33];
+    __shared__ int perm[32];
+    const int tid = threadIdx.x;
+    const int64_t b = blockIdx.y;
+    const uint16_t* tb = t + (n_t == 1 ? 0 : b) * 1024;
+    for (int i = tid; i < 1024; i += 256) lu[i / 32][i % 32] = (double)bf16_bits_to_f32(tb[i]);
+    if (tid < 32) perm[tid] = tid;
+    __syncthreads();
+    for (int k = 0; k < 32; ++k) {
+        // pivot: largest |lu[i][k]| over i >= k (first of equals), by thread 0
+        if (tid == 0) {
+            int p = k;
+            double best = fabs(lu[k][k]);
+            for (int i = k + 1; i < 32; ++i) {
+                const double v = fabs(lu[i][k]);
+                if (v > best) { best = v; p = i; }
+            }
+            if (p != k) {
+                for (int j = 0; j < 32; ++j) {
+                    const double tmp = lu[k][j]; lu[k][j] = lu[p][j]; lu[p][j] = tmp;
+                }
+                const int tp = perm[k]; perm[k] = perm[p]; perm[p] = tp;
+            }
+        }
+        __syncthreads();
+        if (tid > k && tid < 32) lu[tid][k] /= lu[k][k];
+        __syncthreads();
+        for (int e = tid; e < 32 * 32; e += 256) {
+            const int i = e / 32, j = e % 32;
+            if (i > k && j > k) lu[i][j] -= lu[i][k] * lu[k][j];
+        }
+        __syncthreads();
+    }
+    const int64_t n = (int64_t)blockIdx.x * 256 + tid;
+    if (n >= N) return;
+    double v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = (double)w[(b * 32 + perm[i]) * N + n];
+#pragma unroll
+    for (int i = 1; i < 32; ++i)
+#pragma unroll
+        for (int j = 0; j < i; ++j) v[i] -= lu[i][j] * v[j];
+#pragma unroll
+    for (int i = 31; i >= 0; --i) {
+#pragma unroll
+        for (int j = i + 1; j < 32; ++j) v[i] -= lu[i][j] * v[j];
+        v[i] /= lu[i][i];
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) w_out[(b * 32 + i) * N + n] = (float)v[i];
+}
+
+}  // namespace
+
+hipError_t launch_block_transform(const void* x, bool x_bf16, int64_t rows, int64_t cols,
+                                  const uint16_t* t, int64_t n_t, void* y, bool y_bf16,
+                                  uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+    const int64_t nblk = cols / 32;
+    const int64_t wg_cols = (nblk + 15) / 16;                  // 4 waves x 4 blocks per workgroup
+    const int64_t wg_rows = (rows + 32 * kTokIters - 1) / (32 * kTokIters);
+    const dim3 grid((unsigned)wg_cols, (unsigned)wg_rows);
+#define FP4DIT_LAUNCH_BT(XB, YB) \
+    hipLaunchKernelGGL((block_transform_kernel<XB, YB>), grid, dim3(256), 0, stream, x, rows, cols, t, n_t, y, codes, scales)
+    if (x_bf16) {
+        if (y_bf16) FP4DIT_LAUNCH_BT(true, true); else FP4DIT_LAUNCH_BT(true, false);
+    } else {
+        if (y_bf16) FP4DIT_LAUNCH_BT(false, true); else FP4DIT_LAUNCH_BT(false, false);
+    }
+#undef FP4DIT_LAUNCH_BT
+    return hipGetLastError();
+}
+
+hipError_t launch_fold_inverse(const float* w, int64_t K, int64_t N, const uint16_t* t, int64_t n_t,
+                               float* w_out, hipStream_t stream) {
+    const dim3 grid((unsigned)((N + 255) / 256), (unsigned)(K / 32));
+    hipLaunchKernelGGL(fold_inverse_kernel, grid, dim3(256), 0, stream, w, K, N, t, n_t, w_out);
+    return hipGetLastError();
+}
+
+}  // namespace fp4dit

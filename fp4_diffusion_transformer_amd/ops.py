@@ -1,0 +1,215 @@
+"""ctypes binding of libfp4dit.so (include/fp4dit.h).
+
+Argument marshalling only: every step runs in the HIP library.  Tensors must
+be contiguous and on the ROCm device; outputs are allocated with torch and
+filled by the library on torch's current stream.  There is no fallback: if
+the library is missing or a call fails, an exception is raised.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+F32 = 0
+BF16 = 1
+_STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape", 3: "misaligned pointer",
+           4: "unsupported argument", 5: "kernel launch failed"}
+
+_lib_handle = None
+
+
+class Fp4ditError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__("%s failed: %s (%d)" % (fn, _STATUS.get(status, "unknown"), status))
+        self.status = status
+
+
+def library_path():
+    return os.path.join(_HERE, "libfp4dit.so")
+
+
+def lib():
+    """The loaded library with typed entry points (loaded on first use)."""
+    global _lib_handle
+    if _lib_handle is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise Fp4ditError("load", 4) from FileNotFoundError(
+                path + " is not built: run python -m fp4_diffusion_transformer_amd.build")
+        L = ctypes.CDLL(path)
+        P, I64, I32, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+        sig = {
+            "fp4dit_quantize_mxfp4": [P, I32, I64, I64, P, P, P],
+            "fp4dit_block_transform": [P, I32, I64, I64, P, I64, P, I32, P, P, P],
+            "fp4dit_fold_inverse_transform": [P, I64, I64, P, I64, P, P],
+            "fp4dit_pack_weight": [P, I32, I64, I64, I32, P, P, P],
+            "fp4dit_gemm_fp4_epilogue_none": [I64, I64, I64, P, P, P, P, P, I32, P],
+            "fp4dit_gemm_fp4_epilogue_rmsnorm_head": [I64, I64, I64, P, P, P, P, I32, I64, P, F, P, I32, P],
+            "fp4dit_gemm_fp4_epilogue_swiglu": [I64, I64, I64, P, P, P, P, P, I32, P, P, P],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.fp4dit_swiglu_interleave_group.argtypes = []
+        L.fp4dit_swiglu_interleave_group.restype = ctypes.c_int32
+        L.fp4dit_status_string.argtypes = [ctypes.c_int]
+        L.fp4dit_status_string.restype = ctypes.c_char_p
+        _lib_handle = L
+    return _lib_handle
+
+
+def _call(name, *args):
+    st = getattr(lib(), name)(*args)
+    if st != 0:
+        raise Fp4ditError(name, st)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(name + " must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(name + " must be contiguous")
+    return t
+
+
+def _dtype_code(dt):
+    if dt == torch.float32:
+        return F32
+    if dt == torch.bfloat16:
+        return BF16
+    raise ValueError("dtype must be float32 or bfloat16, got %s" % dt)
+
+
+def swiglu_interleave_group():
+    return int(lib().fp4dit_swiglu_interleave_group())
+
+
+def quantize_mxfp4(x, codes=None, scales=None):
+    """x [rows, cols] float32/bfloat16 -> (codes uint8 [rows, cols/2], scales uint8 [rows, cols/32])."""
+    _dev(x, "x")
+    rows, cols = x.shape
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    _call("fp4dit_quantize_mxfp4", _ptr(x), _dtype_code(x.dtype), rows, cols, _ptr(codes), _ptr(scales),
+          _stream())
+    return codes, scales
+
+
+def block_transform(x, t, y_dtype=None, quantize=True, out=None):
+    """y_b = x_b @ T_b per 32-element block.  t: bfloat16 [n_t, 32, 32].
+
+    Returns (y or None, codes or None, scales or None); y is produced when
+    y_dtype (float32 / bfloat16) is given, codes/scales when quantize is set.
+    `out` optionally supplies preallocated (y, codes, scales).
+    """
+    _dev(x, "x")
+    _dev(t, "t")
+    if t.dtype != torch.bfloat16:
+        raise ValueError("t must be bfloat16")
+    rows, cols = x.shape
+    y = codes = scales = None
+    if out is not None:
+        y, codes, scales = out
+    if y_dtype is not None and y is None:
+        y = torch.empty((rows, cols), dtype=y_dtype, device=x.device)
+    if quantize and codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    _call("fp4dit_block_transform", _ptr(x), _dtype_code(x.dtype), rows, cols, _ptr(t), t.shape[0],
+          _ptr(y), _dtype_code(y.dtype) if y is not None else F32, _ptr(codes), _ptr(scales), _stream())
+    return y, codes, scales
+
+
+def fold_inverse_transform(w, t):
+    """W'_b = T_b^-1 @ W_b for the 32-row blocks of w [K, N] float32."""
+    _dev(w, "w")
+    _dev(t, "t")
+    if w.dtype != torch.float32 or t.dtype != torch.bfloat16:
+        raise ValueError("w must be float32 and t bfloat16")
+    k, n = w.shape
+    out = torch.empty_like(w)
+    _call("fp4dit_fold_inverse_transform", _ptr(w), k, n, _ptr(t), t.shape[0], _ptr(out), _stream())
+    return out
+
+
+def pack_weight(w, interleave_group=0):
+    """Logical weight w [K, N] -> MXFP4 codes [N, K/2] and scales [N, K/32].
+
+    interleave_group > 0 treats w as [gate | up] and interleaves the columns
+    for the SwiGLU epilogue (use swiglu_interleave_group()).
+    """
+    _dev(w, "w")
+    k, n = w.shape
+    codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((n, k // 32), dtype=torch.uint8, device=w.device)
+    _call("fp4dit_pack_weight", _ptr(w), _dtype_code(w.dtype), k, n, int(interleave_group), _ptr(codes),
+          _ptr(scales), _stream())
+    return codes, scales
+
+
+def _gemm_shapes(a_codes, a_scales, b_codes, b_scales):
+    for t, nm in ((a_codes, "a_codes"), (a_scales, "a_scales"), (b_codes, "b_codes"), (b_scales, "b_scales")):
+        _dev(t, nm)
+        if t.dtype != torch.uint8:
+            raise ValueError(nm + " must be uint8")
+    m, k2 = a_codes.shape
+    n = b_codes.shape[0]
+    if b_codes.shape[1] != k2:
+        raise ValueError("A and B disagree on K")
+    return m, n, 2 * k2
+
+
+def gemm_fp4_epilogue_none(a_codes, a_scales, b_codes, b_scales, out_dtype=torch.bfloat16, out=None):
+    m, n, k = _gemm_shapes(a_codes, a_scales, b_codes, b_scales)
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a_codes.device)
+    _call("fp4dit_gemm_fp4_epilogue_none", m, n, k, _ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales),
+          _ptr(out), _dtype_code(out.dtype), _stream())
+    return out
+
+
+def gemm_fp4_epilogue_rmsnorm_head(a_codes, a_scales, b_codes, b_scales, head_dim, n_norm_cols, norm_w,
+                                   eps=1e-6, out_dtype=torch.bfloat16, out=None):
+    m, n, k = _gemm_shapes(a_codes, a_scales, b_codes, b_scales)
+    if norm_w is not None:
+        _dev(norm_w, "norm_w")
+        if norm_w.dtype != torch.float32:
+            raise ValueError("norm_w must be float32")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a_codes.device)
+    _call("fp4dit_gemm_fp4_epilogue_rmsnorm_head", m, n, k, _ptr(a_codes), _ptr(a_scales), _ptr(b_codes),
+          _ptr(b_scales), int(head_dim), int(n_norm_cols), _ptr(norm_w), float(eps), _ptr(out),
+          _dtype_code(out.dtype), _stream())
+    return out
+
+
+def gemm_fp4_epilogue_swiglu(a_codes, a_scales, b_codes, b_scales, out_dtype=torch.bfloat16, requant=False,
+                             out=None):
+    """SwiGLU over an interleaved weight: returns (h or None, codes or None, scales or None)."""
+    m, n, k = _gemm_shapes(a_codes, a_scales, b_codes, b_scales)
+    h = codes = scales = None
+    if out is not None:
+        h, codes, scales = out
+    if out_dtype is not None and h is None:
+        h = torch.empty((m, n // 2), dtype=out_dtype, device=a_codes.device)
+    if requant and codes is None:
+        codes = torch.empty((m, n // 4), dtype=torch.uint8, device=a_codes.device)
+        scales = torch.empty((m, n // 64), dtype=torch.uint8, device=a_codes.device)
+    _call("fp4dit_gemm_fp4_epilogue_swiglu", m, n, k, _ptr(a_codes), _ptr(a_scales), _ptr(b_codes),
+          _ptr(b_scales), _ptr(h), _dtype_code(h.dtype) if h is not None else F32, _ptr(codes), _ptr(scales),
+          _stream())
+    return h, codes, scales

@@ -1,0 +1,217 @@
+/*
+ * fp4dit.h - C ABI of libfp4dit.so: the MXFP4 (e2m1 values, one e8m0 scale
+ * per 32 elements) hot path of a diffusion transformer's linear layers on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Every pointer is a DEVICE pointer to memory the caller allocated and
+ *   owns.  The library never allocates, frees, copies to the host or
+ *   synchronises: each call enqueues its kernels on `stream` (the null stream
+ *   is allowed) and returns.  Outputs are valid once the stream reaches them.
+ * - All matrices are dense and row-major, with no leading-dimension padding.
+ * - MXFP4 tensors are a pair (codes, scales):
+ *     codes  uint8 [rows][cols/2]  two e2m1 codes per byte, element 2j in the
+ *                                  low nibble; code = sign<<3 | exp<<1 | mant
+ *                                  with exponent bias 1 (magnitudes 0, 0.5, 1,
+ *                                  1.5, 2, 3, 4, 6);
+ *     scales uint8 [rows][cols/32] e8m0 power-of-two scale 2^(byte - 127) of
+ *                                  each run of 32 consecutive elements of a row.
+ *   The GEMM operands both block along K: A is [M][K], B (the packed weight)
+ *   is [N][K].
+ * - Arguments are checked on the host before anything is enqueued.  A
+ *   status other than FP4DIT_OK means nothing was enqueued, except
+ *   FP4DIT_E_LAUNCH, which reports a failed kernel launch.  No exception
+ *   crosses the ABI; there is no global mutable state, so calls from several
+ *   host threads on different streams are safe.
+ * - Zero-sized work (rows == 0, M == 0) returns FP4DIT_OK and enqueues
+ *   nothing; the other sizes must still be valid.
+ *
+ * Citations name the web pages this library implements: "fal" is the fal
+ * page "Serving sub-second Ideogram v4 without quality loss" (FP4 execution
+ * of a diffusion transformer with the post-GEMM ops fused into the GEMM
+ * epilogue); "KroQuant" is the sns.style summary "KroQuant: efficient
+ * post-training quantisation for diffusion transformers via Kronecker-product
+ * structure".
+ */
+#ifndef FP4DIT_H
+#define FP4DIT_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fp4dit_status {
+    FP4DIT_OK = 0,
+    FP4DIT_E_NULL = 1,        /* a required pointer is NULL                     */
+    FP4DIT_E_SHAPE = 2,       /* a size is negative, too large or not a needed multiple */
+    FP4DIT_E_ALIGN = 3,       /* a pointer is not aligned as the entry point requires   */
+    FP4DIT_E_UNSUPPORTED = 4, /* a dtype, head_dim or option combination not implemented */
+    FP4DIT_E_LAUNCH = 5       /* the kernel launch failed (hipGetLastError)       */
+} fp4dit_status;
+
+typedef enum fp4dit_dtype {
+    FP4DIT_F32 = 0,           /* IEEE binary32                                  */
+    FP4DIT_BF16 = 1           /* bfloat16 (uint16 bit patterns)                 */
+} fp4dit_dtype;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* fp4dit_status_string(fp4dit_status s);
+
+/*
+ * Online activation quantisation to MXFP4.
+ * fal, "Running the transformer in FP4" (the 1-sign / 2-exponent / 1-mantissa
+ * FP4 element); KroQuant, "Deep analysis" (W4A4 in MXFP4).
+ *
+ * x      [rows][cols] of x_dtype (F32 or BF16), 16-byte aligned.
+ * codes  [rows][cols/2], 16-byte aligned;  scales [rows][cols/32].
+ * Per 32-element block: amax = max |x|; shared exponent
+ * s = clamp(floor(log2 amax) - 2, -127, 127) (s = -127 for an all-zero
+ * block); scale byte = s + 127; every element is x / 2^s rounded to the
+ * nearest e2m1 magnitude, ties to even mantissa, saturating at 6, with the
+ * sign bit of x (so -0 gives code 0x8).  A block holding Inf or NaN gets
+ * scale byte 0xFF and zero codes.  Bit-exact: the result is unique.
+ * Requires cols % 32 == 0.
+ */
+fp4dit_status fp4dit_quantize_mxfp4(const void* x, fp4dit_dtype x_dtype,
+                                    int64_t rows, int64_t cols,
+                                    uint8_t* codes, uint8_t* scales,
+                                    hipStream_t stream);
+
+/*
+ * Block-local transform of activations, optionally fused with MXFP4
+ * quantisation of its result.
+ * KroQuant, "Background and overview" (invertible transform on the
+ * activations, inverse on the weights, applied online every step) and "Deep
+ * analysis" (independent 32-element blocks, each with a learned matrix, run
+ * as small-tile matrix-core GEMMs).
+ *
+ * y[r][32b + j] = sum_i x[r][32b + i] * T_b[i][j]   (y_b = x_b . T_b)
+ * x       [rows][cols] of x_dtype (F32 or BF16), 16-byte aligned.
+ * t_bf16  [n_t][32][32] bfloat16, row-major T_b[i][j]; n_t is 1 (one matrix
+ *         for every block) or cols/32 (block b uses T_b).
+ * y       NULL, or [rows][cols] of y_dtype (F32 or BF16, 16-byte aligned):
+ *         the fp32 product, stored (BF16: round to nearest even).
+ * codes, scales  both NULL, or both set: MXFP4 of the fp32 product exactly as
+ *         fp4dit_quantize_mxfp4 would encode it (x never round-trips HBM).
+ * At least one of y / codes must be set.  Products are formed from bf16
+ * operands (an F32 x is rounded to bf16 first) and summed in fp32.
+ * Requires cols % 32 == 0.
+ */
+fp4dit_status fp4dit_block_transform(const void* x, fp4dit_dtype x_dtype,
+                                     int64_t rows, int64_t cols,
+                                     const uint16_t* t_bf16, int64_t n_t,
+                                     void* y, fp4dit_dtype y_dtype,
+                                     uint8_t* codes, uint8_t* scales,
+                                     hipStream_t stream);
+
+/*
+ * Offline weight side of the block transform: W'_b = T_b^-1 . W_b.
+ * KroQuant, "Background and overview" (the inverse transform goes to the
+ * weights).
+ *
+ * w      [K][N] float32, the logical weight of y = x . W; rows 32b..32b+31
+ *        form block b.  w_out [K][N] float32 (may not alias w).
+ * t_bf16, n_t as in fp4dit_block_transform (n_t is 1 or K/32).  Each block
+ * is solved in fp64 by Gaussian elimination with partial pivoting and the
+ * result rounded to fp32.  Returns FP4DIT_E_SHAPE unless K % 32 == 0.
+ * A singular T_b gives non-finite w_out for that block.
+ */
+fp4dit_status fp4dit_fold_inverse_transform(const float* w, int64_t K, int64_t N,
+                                            const uint16_t* t_bf16, int64_t n_t,
+                                            float* w_out, hipStream_t stream);
+
+/*
+ * Offline weight packing: transpose the logical weight to [N][K] and quantise
+ * it to MXFP4 along K (fal, "Running the transformer in FP4"; static FP4
+ * weight quantisation for inference, QAD section).
+ *
+ * w      [K][N] of w_dtype (F32 or BF16), logical y = x . W.
+ * interleave_group  0: no permutation, codes [N][K/2], scales [N][K/32].
+ *        g > 0: SwiGLU weight (fal, "Fusing gated SiLU"): w holds
+ *        [gate | up], N/2 columns each; physical column p takes logical
+ *        output j = (p / 2g) * g + p % g from the up half if (p / g) is odd,
+ *        else from the gate half, so gate and up outputs sit next to each
+ *        other in the GEMM's output tile.  g must equal
+ *        fp4dit_swiglu_interleave_group() for use with
+ *        fp4dit_gemm_fp4_epilogue_swiglu, and N % (2g) == 0.
+ * Same encoding as fp4dit_quantize_mxfp4.  Requires K % 32 == 0.
+ */
+fp4dit_status fp4dit_pack_weight(const void* w, fp4dit_dtype w_dtype,
+                                 int64_t K, int64_t N, int32_t interleave_group,
+                                 uint8_t* codes, uint8_t* scales,
+                                 hipStream_t stream);
+
+/* Interleave group size g the SwiGLU epilogue expects (see fp4dit_pack_weight). */
+int32_t fp4dit_swiglu_interleave_group(void);
+
+/*
+ * The GEMM shared by the three fused entry points below
+ * (fal, section on epilogue fusion: A . B formed tile by tile with on-chip
+ * fp32 accumulators; the epilogue runs before the one store to HBM):
+ *     C[m][n] = sum_k D(A)[m][k] * D(B)[n][k]
+ * with D() the exact MXFP4 value, scaled FP4 matrix-core products and fp32
+ * accumulation.  Shapes: a_codes [M][K/2], a_scales [M][K/32], b_codes
+ * [N][K/2], b_scales [N][K/32]; every codes pointer 16-byte aligned, every
+ * scales pointer 4-byte aligned.  Requires K % 256 == 0 and K > 0,
+ * N % 256 == 0 and N > 0, and M*K/2 and N*K/2 below 2^31 bytes; M >= 0 is
+ * otherwise arbitrary (a ragged last token tile is masked).
+ */
+
+/*
+ * No epilogue: out [M][N] = C, stored as out_dtype (F32, or BF16 rounded to
+ * nearest even).  out 16-byte aligned.  fal, epilogue-fusion section (cast).
+ */
+fp4dit_status fp4dit_gemm_fp4_epilogue_none(int64_t M, int64_t N, int64_t K,
+                                            const uint8_t* a_codes, const uint8_t* a_scales,
+                                            const uint8_t* b_codes, const uint8_t* b_scales,
+                                            void* out, fp4dit_dtype out_dtype,
+                                            hipStream_t stream);
+
+/*
+ * Per-head RMSNorm epilogue (fal, epilogue-fusion section and "Why
+ * head_dim=256 is hard" / "Revisit fusion"): for every row and every head of
+ * head_dim contiguous columns below n_norm_cols,
+ *     y = C * rsqrt(mean(C^2 over the head) + eps) * norm_w[column],
+ * with the statistics taken from the fp32 accumulators; columns at or past
+ * n_norm_cols are stored unchanged (e.g. the V part of a fused QKV).
+ * head_dim is 128 or 256; n_norm_cols % head_dim == 0, 0 <= n_norm_cols <= N;
+ * norm_w [n_norm_cols] float32, 16-byte aligned (may be NULL only if
+ * n_norm_cols == 0); eps >= 0 and finite.  out [M][N] of out_dtype,
+ * 16-byte aligned.
+ */
+fp4dit_status fp4dit_gemm_fp4_epilogue_rmsnorm_head(int64_t M, int64_t N, int64_t K,
+                                                    const uint8_t* a_codes, const uint8_t* a_scales,
+                                                    const uint8_t* b_codes, const uint8_t* b_scales,
+                                                    int32_t head_dim, int64_t n_norm_cols,
+                                                    const float* norm_w, float eps,
+                                                    void* out, fp4dit_dtype out_dtype,
+                                                    hipStream_t stream);
+
+/*
+ * SwiGLU epilogue (fal, "Fusing gated SiLU"): with B packed by
+ * fp4dit_pack_weight(..., fp4dit_swiglu_interleave_group(), ...) from
+ * [gate | up], N physical columns give N/2 outputs
+ *     h[m][j] = silu(gate[m][j]) * up[m][j],  silu(z) = z / (1 + exp(-z)).
+ * out        NULL, or [M][N/2] of out_dtype (16-byte aligned).
+ * out_codes, out_scales  both NULL, or both set: MXFP4 re-quantisation of
+ *            the fp32 h along its columns ([M][N/4] codes, 16-byte aligned,
+ *            and [M][N/64] scales), encoded as fp4dit_quantize_mxfp4 does.
+ * At least one output must be set.
+ */
+fp4dit_status fp4dit_gemm_fp4_epilogue_swiglu(int64_t M, int64_t N, int64_t K,
+                                              const uint8_t* a_codes, const uint8_t* a_scales,
+                                              const uint8_t* b_codes, const uint8_t* b_scales,
+                                              void* out, fp4dit_dtype out_dtype,
+                                              uint8_t* out_codes, uint8_t* out_scales,
+                                              hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4DIT_H */

@@ -1,0 +1,98 @@
+"""Comparison rules between the HIP path and the CPU oracle.
+
+Values: err_i = |g_i - r_i| / max(|r_i|, 0.1 * RMS(r over the row, or over
+the row's head)), so cancellation near zero does not blow up the relative
+error.  Bars: 2e-3 for fp32 stores, 1e-2 after a bf16 store (fp32
+accumulation of K products of magnitude ~1 differs from float64 by about
+sqrt(K) * 2**-24 of the row RMS, some 100x below the bars; bf16 rounding
+alone is 2**-9 relative).
+
+Codes: plain quantisation of given inputs has exactly one correct result and
+is compared bit for bit.  Where the value being quantised is itself an fp32
+sum (transform output, SwiGLU output), a code may differ from the float64
+oracle only where the oracle's scaled value lies within TAU of a rounding
+midpoint, and a block scale only where the block amax lies within relative
+AMAX_REL of a power of two (then the whole block is excused).  fp32 sums are
+off by ~1e-5 in scaled units, so TAU leaves a ~10x margin; everything else
+must match exactly.
+"""
+
+import numpy as np
+
+from oracle import mxfp4
+
+TAU = 1e-4
+AMAX_REL = 1e-5
+TOL_F32 = 2e-3
+TOL_BF16 = 1e-2
+
+
+def rel_err(gpu, ref, group=None):
+    """Max S14-style relative error; group = columns per RMS group (None: whole row)."""
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    m, n = r.shape
+    grp = n if group is None else group
+    rr = r.reshape(m, n // grp, grp)
+    rms = np.sqrt(np.mean(rr * rr, axis=2, keepdims=True))
+    floor = np.broadcast_to(0.1 * rms, rr.shape).reshape(m, n)
+    denom = np.maximum(np.abs(r), floor)
+    denom = np.where(denom == 0, 1.0, denom)
+    return float(np.max(np.abs(g - r) / denom))
+
+
+def assert_close(gpu, ref, tol, group=None, what=""):
+    e = rel_err(gpu, ref, group)
+    assert e <= tol, "%s: max relative error %.3e > %.1e" % (what, e, tol)
+    return e
+
+
+def unpack(packed):
+    return mxfp4.unpack_codes(np.asarray(packed, dtype=np.uint8))
+
+
+def assert_codes_exact(gpu_packed, gpu_scales, ref_codes, ref_scales, what=""):
+    gc = unpack(gpu_packed)
+    gs = np.asarray(gpu_scales, dtype=np.uint8)
+    bad_s = np.argwhere(gs != ref_scales)
+    assert bad_s.size == 0, "%s: %d scale mismatches, first at %s: gpu %d ref %d" % (
+        what, len(bad_s), bad_s[0], gs[tuple(bad_s[0])], ref_scales[tuple(bad_s[0])])
+    bad = np.argwhere(gc != ref_codes)
+    assert bad.size == 0, "%s: %d code mismatches, first at %s: gpu %d ref %d" % (
+        what, len(bad), bad[0], gc[tuple(bad[0])], ref_codes[tuple(bad[0])])
+
+
+def _near_midpoint(q):
+    a = np.abs(q)
+    d = np.min(np.abs(a[..., None] - mxfp4.E2M1_MIDPOINTS[None, None, :]), axis=-1)
+    return d <= TAU
+
+
+def _near_pow2(amax):
+    with np.errstate(divide="ignore"):
+        e = np.round(np.log2(np.where(amax > 0, amax, 1.0)))
+    return np.abs(amax / 2.0 ** e - 1.0) <= AMAX_REL
+
+
+def assert_codes_banded(gpu_packed, gpu_scales, ref_values, what=""):
+    """Codes of fp32 sums vs the float64 oracle values, with the excusal band.
+
+    Returns (excused_codes, excused_blocks) counts."""
+    ref_values = np.asarray(ref_values, dtype=np.float64)
+    rc, rs, q = mxfp4.quantize(ref_values, return_scaled=True)
+    gc = unpack(gpu_packed)
+    gs = np.asarray(gpu_scales, dtype=np.uint8)
+    m, n = ref_values.shape
+    amax = np.max(np.abs(ref_values.reshape(m, n // 32, 32)), axis=2)
+    scale_bad = gs != rs
+    scale_ok_excuse = _near_pow2(amax)
+    unexcused_scale = scale_bad & ~scale_ok_excuse
+    assert not unexcused_scale.any(), "%s: %d unexcused scale mismatches at %s" % (
+        what, int(unexcused_scale.sum()), np.argwhere(unexcused_scale)[0])
+    block_excused = np.repeat(scale_bad, 32, axis=1)
+    code_bad = (gc != rc) & ~block_excused
+    unexcused = code_bad & ~_near_midpoint(q)
+    assert not unexcused.any(), "%s: %d unexcused code mismatches, first %s (ref q=%r)" % (
+        what, int(unexcused.sum()), np.argwhere(unexcused)[0], q[tuple(np.argwhere(unexcused)[0])])
+    return int(code_bad.sum()), int(scale_bad.sum())

@@ -1,0 +1,111 @@
+"""The C-ABI library loads, exports what include/fp4dit.h declares, and
+rejects bad arguments on the host (no GPU needed: nothing is launched).
+
+Every call below carries at least one invalid argument, so validation
+returns before any HIP call; the fake addresses are never dereferenced."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp4_diffusion_transformer_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4dit.h")
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_UNSUP = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+P = 0x10000          # a fake, 64 KiB-aligned "device" address: never dereferenced
+P_ODD = 0x10001
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp4dit_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ops.library_path()):
+        pytest.fail("libfp4dit.so is not built (python -m fp4_diffusion_transformer_amd.build)")
+    return ops.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) == 9
+    raw = ctypes.CDLL(ops.library_path())
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_status_strings_and_group(L):
+    assert L.fp4dit_status_string(0) == b"ok"
+    assert L.fp4dit_status_string(2) == b"invalid shape"
+    assert L.fp4dit_swiglu_interleave_group() == 32
+
+
+def test_quantize_validation(L):
+    q = L.fp4dit_quantize_mxfp4
+    assert q(P, F32, 4, 48, P, P, None) == E_SHAPE           # cols % 32
+    assert q(P, F32, -1, 64, P, P, None) == E_SHAPE
+    assert q(P, 7, 4, 64, P, P, None) == E_UNSUP             # dtype
+    assert q(None, BF16, 4, 64, P, P, None) == E_NULL
+    assert q(P, BF16, 4, 64, None, P, None) == E_NULL
+    assert q(P_ODD, BF16, 4, 64, P, P, None) == E_ALIGN
+    assert q(P, BF16, 4, 64, P_ODD, P, None) == E_ALIGN
+    assert q(None, BF16, 0, 64, None, None, None) == OK       # empty: nothing to do
+
+
+def test_gemm_validation(L):
+    g = L.fp4dit_gemm_fp4_epilogue_none
+    assert g(256, 500, 512, P, P, P, P, P, BF16, None) == E_SHAPE         # N % 256
+    assert g(256, 512, 384, P, P, P, P, P, BF16, None) == E_SHAPE         # K % 256
+    assert g(256, 512, 0, P, P, P, P, P, BF16, None) == E_SHAPE
+    assert g(-1, 512, 512, P, P, P, P, P, BF16, None) == E_SHAPE
+    assert g(256, 512, 512, None, P, P, P, P, BF16, None) == E_NULL
+    assert g(256, 512, 512, P, P, P, P, None, BF16, None) == E_NULL
+    assert g(256, 512, 512, P_ODD, P, P, P, P, BF16, None) == E_ALIGN
+    assert g(256, 512, 512, P, P + 2, P, P, P, BF16, None) == E_ALIGN      # scales need 4 bytes
+    assert g(256, 512, 512, P, P, P, P, P, 9, None) == E_UNSUP
+    assert g(0, 512, 512, None, None, None, None, None, BF16, None) == OK
+    assert g(1 << 20, 512, 8192, P, P, P, P, P, BF16, None) == E_SHAPE     # 32-bit operand offsets
+
+
+def test_rmsnorm_validation(L):
+    r = L.fp4dit_gemm_fp4_epilogue_rmsnorm_head
+    args = (256, 512, 512, P, P, P, P)
+    assert r(*args, 64, 512, P, 1e-6, P, BF16, None) == E_UNSUP            # head_dim
+    assert r(*args, 256, 384, P, 1e-6, P, BF16, None) == E_SHAPE           # n_norm % head_dim
+    assert r(*args, 128, 640, P, 1e-6, P, BF16, None) == E_SHAPE           # n_norm > N
+    assert r(*args, 128, 512, None, 1e-6, P, BF16, None) == E_NULL
+    assert r(*args, 128, 512, P + 4, 1e-6, P, BF16, None) == E_ALIGN
+    assert r(*args, 128, 512, P, -1.0, P, BF16, None) == E_UNSUP           # eps < 0
+    assert r(*args, 128, 512, P, float("nan"), P, BF16, None) == E_UNSUP
+
+
+def test_swiglu_validation(L):
+    s = L.fp4dit_gemm_fp4_epilogue_swiglu
+    args = (256, 512, 512, P, P, P, P)
+    assert s(*args, None, BF16, None, None, None) == E_NULL                # no output at all
+    assert s(*args, None, BF16, P, None, None) == E_UNSUP                  # codes without scales
+    assert s(*args, P_ODD, BF16, None, None, None) == E_ALIGN
+
+
+def test_transform_pack_fold_validation(L):
+    bt = L.fp4dit_block_transform
+    assert bt(P, BF16, 8, 96, P, 2, P, F32, None, None, None) == E_SHAPE   # n_t not 1 or cols/32
+    assert bt(P, BF16, 8, 96, P, 3, None, F32, None, None, None) == E_NULL  # no output
+    assert bt(P, BF16, 8, 96, P, 1, None, F32, P, None, None) == E_UNSUP   # codes without scales
+    assert bt(P, BF16, 8, 80, P, 1, P, F32, None, None, None) == E_SHAPE
+    pw = L.fp4dit_pack_weight
+    assert pw(P, F32, 64, 96, 32, P, P, None) == E_SHAPE                   # N % 2g
+    assert pw(P, F32, 48, 64, 0, P, P, None) == E_SHAPE                    # K % 32
+    assert pw(P, F32, 64, 64, -1, P, P, None) == E_UNSUP
+    fo = L.fp4dit_fold_inverse_transform
+    assert fo(P, 64, 16, P, 3, P + 64, None) == E_SHAPE
+    assert fo(P, 64, 16, P, 2, P, None) == E_UNSUP                          # aliasing
+    assert fo(None, 64, 16, P, 2, P + 64, None) == E_NULL

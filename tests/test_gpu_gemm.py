@@ -1,0 +1,158 @@
+"""GPU parity of the fused MXFP4 GEMM + epilogues against the oracle.
+
+Operands are MXFP4 codes produced by the oracle's quantiser from seeded
+inputs, so these tests isolate the GEMM and its epilogues.  Shapes span
+several workgroup tiles and a ragged last token tile.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import parity
+from gpu_util import announce, dev, dev_u8, host
+from fp4_diffusion_transformer_amd import ops
+from oracle import bf16 as obf16
+from oracle import gemm as ogemm
+from oracle import mxfp4
+
+pytestmark = pytest.mark.gpu
+
+
+def _operands(rng, m, n, k, spread=True):
+    x = rng.standard_normal((m, k))
+    if spread:
+        x *= 2.0 ** rng.integers(-3, 4, (m, 1))
+    w = rng.standard_normal((n, k)) / np.sqrt(k)
+    ac, as_ = mxfp4.quantize(x)
+    bc, bs = mxfp4.quantize(w)
+    return ac, as_, bc, bs
+
+
+def _dev_ops(ac, as_, bc, bs):
+    return (dev_u8(mxfp4.pack_codes(ac)), dev_u8(as_), dev_u8(mxfp4.pack_codes(bc)), dev_u8(bs))
+
+
+def test_exact_on_representable_inputs():
+    """Grid values with equal scales: every partial sum is exact in fp32, so
+    the fp32 output must equal the oracle bit for bit."""
+    rng = np.random.default_rng(0)
+    m, n, k = 300, 512, 4096
+    ac = rng.integers(0, 16, (m, k)).astype(np.uint8)
+    bc = rng.integers(0, 16, (n, k)).astype(np.uint8)
+    as_ = np.full((m, k // 32), 127, np.uint8)
+    bs = np.full((n, k // 32), 127, np.uint8)
+    ref = ogemm.gemm(ac, as_, bc, bs)
+    announce("gemm none exact", m, n, k)
+    out = ops.gemm_fp4_epilogue_none(*_dev_ops(ac, as_, bc, bs), out_dtype=torch.float32)
+    assert np.array_equal(host(out).astype(np.float64), ref)
+
+
+def test_scales_apply_per_block_and_operand():
+    """Distinct scale per (row, K-block) on each side, exact products: any
+    mix-up of the scale bytes between K-steps, lane groups or operands shows."""
+    rng = np.random.default_rng(1)
+    m, n, k = 64, 256, 1024
+    ac = rng.integers(0, 16, (m, k)).astype(np.uint8)
+    bc = rng.integers(0, 16, (n, k)).astype(np.uint8)
+    as_ = rng.integers(124, 131, (m, k // 32)).astype(np.uint8)
+    bs = rng.integers(124, 131, (n, k // 32)).astype(np.uint8)
+    ref = ogemm.gemm(ac, as_, bc, bs)
+    announce("gemm none scales", m, n, k)
+    out = ops.gemm_fp4_epilogue_none(*_dev_ops(ac, as_, bc, bs), out_dtype=torch.float32)
+    parity.assert_close(host(out), ref, 1e-5, what="per-block scales")
+
+
+@pytest.mark.parametrize("m", [1, 255, 256, 257, 600])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_none_random(m, out_dtype):
+    rng = np.random.default_rng(m)
+    n, k = 768, 768
+    ac, as_, bc, bs = _operands(rng, m, n, k)
+    ref = ogemm.gemm(ac, as_, bc, bs)
+    announce("gemm none", m, n, k, out_dtype)
+    out = ops.gemm_fp4_epilogue_none(*_dev_ops(ac, as_, bc, bs), out_dtype=out_dtype)
+    tol = parity.TOL_F32 if out_dtype == torch.float32 else parity.TOL_BF16
+    parity.assert_close(host(out), ref, tol, what="none")
+    if out_dtype == torch.bfloat16:
+        # within one bf16 rounding of the RNE-rounded reference
+        assert np.max(np.abs(host(out) - obf16.round_bf16(ref)) / np.maximum(np.abs(ref), 1e-3)) < 2 ** -7
+
+
+@pytest.mark.parametrize("head_dim,n,n_norm", [(128, 768, 512), (128, 768, 384), (128, 512, 0),
+                                              (256, 768, 512), (256, 512, 256)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_rmsnorm_head(head_dim, n, n_norm, out_dtype):
+    rng = np.random.default_rng(head_dim + n + n_norm)
+    m, k = 300, 512
+    ac, as_, bc, bs = _operands(rng, m, n, k)
+    norm_w = rng.uniform(0.5, 1.5, n_norm).astype(np.float32)
+    eps = 1e-6
+    c = ogemm.gemm(ac, as_, bc, bs)
+    ref = ogemm.rmsnorm_head(c, head_dim, n_norm, norm_w.astype(np.float64), eps)
+    announce("gemm rmsnorm", head_dim, n, n_norm, out_dtype)
+    out = ops.gemm_fp4_epilogue_rmsnorm_head(*_dev_ops(ac, as_, bc, bs), head_dim, n_norm,
+                                             dev(norm_w, torch.float32) if n_norm else None, eps,
+                                             out_dtype=out_dtype)
+    tol = parity.TOL_F32 if out_dtype == torch.float32 else parity.TOL_BF16
+    parity.assert_close(host(out), ref, tol, group=head_dim, what="rmsnorm hd%d" % head_dim)
+
+
+def test_rmsnorm_eps_dominates_tiny_heads():
+    """Heads whose accumulators are tiny: the eps term decides the scale."""
+    rng = np.random.default_rng(3)
+    m, n, k = 64, 256, 256
+    ac, as_, bc, bs = _operands(rng, m, n, k, spread=False)
+    as_ = np.full_like(as_, 127 - 12)            # accumulators ~2**-12
+    norm_w = np.ones(n, np.float32)
+    eps = 1e-6
+    ref = ogemm.rmsnorm_head(ogemm.gemm(ac, as_, bc, bs), 128, n, norm_w.astype(np.float64), eps)
+    announce("gemm rmsnorm tiny heads")
+    out = ops.gemm_fp4_epilogue_rmsnorm_head(*_dev_ops(ac, as_, bc, bs), 128, n, dev(norm_w, torch.float32),
+                                             eps, out_dtype=torch.float32)
+    parity.assert_close(host(out), ref, parity.TOL_F32, group=128, what="tiny heads")
+
+
+def _swiglu_operands(rng, m, n_half, k):
+    x = rng.standard_normal((m, k)) * 2.0 ** rng.integers(-2, 3, (m, 1))
+    wg = rng.standard_normal((k, n_half)) / np.sqrt(k) * 2
+    wu = rng.standard_normal((k, n_half)) / np.sqrt(k)
+    ac, as_ = mxfp4.quantize(x)
+    gc_, gs_ = mxfp4.quantize(wg.T)
+    uc_, us_ = mxfp4.quantize(wu.T)
+    g = ops.swiglu_interleave_group()
+    # physical weight rows: the oracle's codes of the logical columns, interleaved
+    pair, is_up = ogemm.interleave_columns(n_half, g)
+    bc = np.where(is_up[:, None], uc_[pair], gc_[pair])
+    bs = np.where(is_up[:, None], us_[pair], gs_[pair])
+    c_g = ogemm.gemm(ac, as_, gc_, gs_)
+    c_u = ogemm.gemm(ac, as_, uc_, us_)
+    return (ac, as_, bc, bs), ogemm.swiglu(c_g, c_u)
+
+
+@pytest.mark.parametrize("m", [300, 1])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_swiglu_values(m, out_dtype):
+    rng = np.random.default_rng(11 + m)
+    operands, h_ref = _swiglu_operands(rng, m, 384, 512)
+    announce("gemm swiglu", m, out_dtype)
+    h, codes, scales = ops.gemm_fp4_epilogue_swiglu(*_dev_ops(*operands), out_dtype=out_dtype, requant=False)
+    assert codes is None
+    tol = parity.TOL_F32 if out_dtype == torch.float32 else parity.TOL_BF16
+    parity.assert_close(host(h), h_ref, tol, what="swiglu")
+
+
+@pytest.mark.parametrize("with_bf16", [False, True])
+def test_swiglu_requant(with_bf16):
+    rng = np.random.default_rng(21)
+    operands, h_ref = _swiglu_operands(rng, 300, 512, 768)
+    announce("gemm swiglu requant", with_bf16)
+    h, codes, scales = ops.gemm_fp4_epilogue_swiglu(*_dev_ops(*operands),
+                                                    out_dtype=torch.bfloat16 if with_bf16 else None,
+                                                    requant=True)
+    if with_bf16:
+        parity.assert_close(host(h), h_ref, parity.TOL_BF16, what="swiglu bf16 + requant")
+    else:
+        assert h is None
+    exc_codes, exc_blocks = parity.assert_codes_banded(host(codes), host(scales), h_ref, "swiglu requant")
+    assert exc_codes <= 0.001 * h_ref.size

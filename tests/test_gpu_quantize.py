@@ -1,0 +1,110 @@
+"""GPU parity of the MXFP4 quantisation and weight-packing kernels.
+
+Quantising given values has exactly one correct result, so codes and scales
+are compared bit for bit with the oracle (bf16 and fp32 inputs, every finite
+bf16 value, hand-worked blocks, ragged and empty inputs).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import golden_io
+import parity
+from gpu_util import announce, dev, dev_u8, host
+from fp4_diffusion_transformer_amd import ops, workloads
+from oracle import gemm as ogemm
+from oracle import mxfp4
+
+pytestmark = pytest.mark.gpu
+
+
+def _quant_both(x64, dtype):
+    announce("quantize", x64.shape, dtype)
+    codes, scales = ops.quantize_mxfp4(dev(x64, dtype))
+    torch.cuda.synchronize()
+    return host(codes), host(scales)
+
+
+def test_hand_worked_blocks_fp32_and_bf16():
+    blocks = golden_io.mxfp4_blocks()
+    x = np.array([b[1] for b in blocks])
+    for dtype in (torch.float32, torch.bfloat16):
+        gc, gs = _quant_both(x, dtype)
+        for i, (name, _, scale, packed) in enumerate(blocks):
+            assert int(gs[i, 0]) == scale, (name, dtype)
+            assert gc[i].tolist() == packed, (name, dtype)
+
+
+def test_every_bf16_value():
+    bits = np.arange(65536, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32)
+    vals = vals[np.isfinite(vals)].astype(np.float64)
+    rows = []
+    for d in (0, 1, 2, 3):                     # companions 2**d above each binade
+        comp = np.where(vals != 0, np.ldexp(1.0, np.frexp(np.abs(vals))[1] + d), 0.0)
+        comp = np.where(np.isfinite(comp) & (comp <= 2.0 ** 127), comp, 0.0)
+        blk = np.zeros((len(vals), 32))
+        blk[:, 0] = vals
+        blk[:, 1] = comp
+        rows.append(blk)
+    x = np.concatenate(rows)
+    x = x[: (len(x) // 8) * 8].reshape(-1, 256)   # 8 blocks per row
+    rc, rs = mxfp4.quantize(x)
+    gc, gs = _quant_both(x, torch.bfloat16)
+    parity.assert_codes_exact(gc, gs, rc, rs, "all bf16")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("rows,cols", [(1, 32), (3, 96), (257, 3072), (1000, 512)])
+def test_random_with_outliers(dtype, rows, cols):
+    rng = np.random.default_rng(rows * 7 + cols)
+    x = rng.standard_normal((rows, cols)) * 2.0 ** rng.integers(-30, 30, (rows, 1))
+    x[:, rng.choice(cols, max(1, cols // 200), replace=False)] *= 20
+    x[0, :7] = [0.0, -0.0, 1e-40, -1e-42, 6.0, -5.0, 0.25]
+    x = x.astype(np.float32)
+    if dtype == torch.bfloat16:
+        x = workloads.to_bf16_values(x)
+    x = x.astype(np.float64)
+    rc, rs = mxfp4.quantize(x)
+    gc, gs = _quant_both(x, dtype)
+    parity.assert_codes_exact(gc, gs, rc, rs, "random %s" % dtype)
+
+
+def test_empty_rows_is_a_no_op():
+    x = torch.zeros((0, 64), device="cuda", dtype=torch.bfloat16)
+    codes, scales = ops.quantize_mxfp4(x)
+    assert codes.shape == (0, 32) and scales.shape == (0, 2)
+
+
+def test_workload_activations_bit_exact():
+    w = workloads.qkv_hd128(rows=4096)
+    rc, rs = mxfp4.quantize(w.x.astype(np.float64))
+    gc, gs = _quant_both(w.x.astype(np.float64), torch.bfloat16)
+    parity.assert_codes_exact(gc, gs, rc, rs, "qkv activations 4096x3072")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_pack_weight_plain(dtype):
+    rng = np.random.default_rng(5)
+    k, n = 512, 320
+    w = rng.standard_normal((k, n)).astype(np.float32) / 20
+    if dtype == torch.bfloat16:
+        w = workloads.to_bf16_values(w)
+    announce("pack_weight", k, n, dtype)
+    gc, gs = ops.pack_weight(dev(w, dtype))
+    rc, rs = mxfp4.quantize(w.astype(np.float64).T)
+    parity.assert_codes_exact(host(gc), host(gs), rc, rs, "pack plain")
+
+
+def test_pack_weight_swiglu_interleave():
+    rng = np.random.default_rng(6)
+    k, n_half = 256, 256
+    wg = rng.standard_normal((k, n_half)).astype(np.float32)
+    wu = rng.standard_normal((k, n_half)).astype(np.float32) * 3
+    g = ops.swiglu_interleave_group()
+    announce("pack_weight swiglu", k, 2 * n_half, g)
+    gc, gs = ops.pack_weight(dev(np.concatenate([wg, wu], axis=1), torch.float32), interleave_group=g)
+    phys = ogemm.interleave_weight(wg, wu, g)
+    rc, rs = mxfp4.quantize(phys.astype(np.float64).T)
+    parity.assert_codes_exact(host(gc), host(gs), rc, rs, "pack interleaved")

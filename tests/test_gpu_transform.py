@@ -1,0 +1,71 @@
+"""GPU parity of the block transform (+ fused quantise) and the weight fold."""
+
+import numpy as np
+import pytest
+import torch
+
+import parity
+from gpu_util import announce, dev, host
+from fp4_diffusion_transformer_amd import ops, workloads
+from oracle import mxfp4, transform
+
+pytestmark = pytest.mark.gpu
+
+
+def _t(n_t, seed):
+    return workloads.transforms(seed, n_t)
+
+
+@pytest.mark.parametrize("rows,cols,n_t", [(300, 512, 16), (300, 512, 1), (1, 96, 3), (129, 160, 5)])
+@pytest.mark.parametrize("x_dtype", [torch.bfloat16, torch.float32])
+def test_transform_values(rows, cols, n_t, x_dtype):
+    rng = np.random.default_rng(rows + cols + n_t)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x[:, rng.choice(cols, 2, replace=False)] *= 20
+    xb = workloads.to_bf16_values(x)               # the kernel multiplies bf16 operands
+    t = _t(n_t, 40 + n_t)
+    ref = transform.block_transform(xb.astype(np.float64), t.astype(np.float64))
+    announce("block_transform values", rows, cols, n_t, x_dtype)
+    xin = xb if x_dtype == torch.bfloat16 else x
+    y, codes, scales = ops.block_transform(dev(xin, x_dtype), dev(t, torch.bfloat16), y_dtype=torch.float32,
+                                           quantize=True)
+    parity.assert_close(host(y), ref, 1e-5, what="transform fp32 y")
+    exc, blk = parity.assert_codes_banded(host(codes), host(scales), ref, "transform codes")
+    assert exc <= 0.001 * ref.size
+
+
+def test_transform_bf16_y_only():
+    rng = np.random.default_rng(9)
+    x = workloads.to_bf16_values(rng.standard_normal((64, 256)).astype(np.float32))
+    t = _t(8, 9)
+    ref = transform.block_transform(x.astype(np.float64), t.astype(np.float64))
+    announce("block_transform bf16 y")
+    y, codes, scales = ops.block_transform(dev(x, torch.bfloat16), dev(t, torch.bfloat16),
+                                           y_dtype=torch.bfloat16, quantize=False)
+    assert codes is None
+    parity.assert_close(host(y), ref, parity.TOL_BF16, what="transform bf16 y")
+
+
+def test_identity_transform_equals_plain_quantize():
+    """T = I: the fused transform+quantise must give the plain quantiser's
+    codes bit for bit (the product is exact)."""
+    rng = np.random.default_rng(10)
+    x = workloads.to_bf16_values((rng.standard_normal((200, 384)) * 3).astype(np.float32)).astype(np.float64)
+    t = np.broadcast_to(np.eye(32, dtype=np.float32), (1, 32, 32)).copy()
+    rc, rs = mxfp4.quantize(x)
+    announce("block_transform identity")
+    _, codes, scales = ops.block_transform(dev(x, torch.bfloat16), dev(t, torch.bfloat16), quantize=True)
+    parity.assert_codes_exact(host(codes), host(scales), rc, rs, "identity transform")
+
+
+def test_fold_inverse():
+    rng = np.random.default_rng(12)
+    k, n = 256, 300
+    w = (rng.standard_normal((k, n)) / 16).astype(np.float32)
+    for n_t in (1, k // 32):
+        t = _t(n_t, 70 + n_t)
+        ref = transform.fold_inverse(w.astype(np.float64), t.astype(np.float64))
+        announce("fold_inverse", k, n, n_t)
+        got = host(ops.fold_inverse_transform(dev(w, torch.float32), dev(t, torch.bfloat16)))
+        # fp64 solve rounded to fp32: within a couple of fp32 ulps of the oracle
+        assert np.max(np.abs(got - ref) / np.maximum(np.abs(ref), 1e-3)) < 1e-6
