@@ -1,0 +1,331 @@
+"""Benchmark of the fused MXFP4 GEMM + epilogue hot path on one MI355X.
+
+One step = one pass of the hot path over one batch of synthetic DiT inputs:
+online MXFP4 quantisation of each layer's activations, then the fused FP4
+GEMM with its epilogue, for every linear of the workload.  Inputs are
+resident in HBM before the timed region; activation buffers rotate over
+several copies (more than the 256 MB last-level cache) so the quantiser reads
+HBM, while the packed weights stay cache-warm as they would in serving.
+
+Workloads (seeded synthetic tensors, random-init weights):
+  dit_1k_linears (default)  one 1K image (4096 tokens): QKV 3072->9216 with
+                            per-head RMSNorm hd 128 on Q,K; QKV 4096->12288 with
+                            RMSNorm hd 256; FFN up 3072->2x12288 with SwiGLU and
+                            MXFP4 re-quantisation of the output.
+  dit_block                 batch of 4 images (16384 tokens): block transform +
+                            quantise of every input, QKV (RMSNorm hd 128), FFN up
+                            (SwiGLU, bf16 out), FFN down (no epilogue).
+
+Prints one JSON line.  TFLOP/s counts 2*M*N*K per GEMM (N the physical width).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_MXFP4_TFLOPS = 10100.0     # MI355X dense MXFP4 matrix peak
+PEAK_HBM_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="dit_1k_linears", choices=["dit_1k_linears", "dit_block"])
+    p.add_argument("--rotate", type=int, default=4, help="activation buffer copies cycled over steps")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+# ------------------------------------------------------------------ layers --
+class Layer:
+    """One fused linear: activations -> [transform +] quantise -> GEMM + epilogue."""
+
+    def __init__(self, name, wl, ops, torch, rotate, x_override=None, transform=None):
+        self.name, self.wl = name, wl
+        dev = "cuda"
+        self.m, self.k = wl.m, wl.k
+        x = wl.x if x_override is None else x_override
+        xs = [torch.from_numpy(x).to(dev, torch.bfloat16)]
+        for r in range(1, rotate):                     # distinct copies defeat the LLC
+            xs.append(xs[0].clone())
+        self.xs = xs
+        self.t = None if transform is None else torch.from_numpy(transform).to(dev, torch.bfloat16)
+        if wl.epilogue == "swiglu":
+            w = np.concatenate([wl.w_gate, wl.w_up], axis=1)
+            group = ops.swiglu_interleave_group()
+        else:
+            w = wl.w
+            group = 0
+        wd = torch.from_numpy(w).to(dev, torch.float32)
+        if self.t is not None:
+            wd = ops.fold_inverse_transform(wd, self.t)
+        self.b_codes, self.b_scales = ops.pack_weight(wd, interleave_group=group)
+        del wd
+        self.n = self.b_codes.shape[0]
+        self.a_codes = torch.empty((self.m, self.k // 2), dtype=torch.uint8, device=dev)
+        self.a_scales = torch.empty((self.m, self.k // 32), dtype=torch.uint8, device=dev)
+        if wl.epilogue == "swiglu":
+            self.out = torch.empty((self.m, self.n // 2), dtype=torch.bfloat16, device=dev) \
+                if not wl.requant else None
+            self.codes = torch.empty((self.m, self.n // 4), dtype=torch.uint8, device=dev) if wl.requant else None
+            self.scales = torch.empty((self.m, self.n // 64), dtype=torch.uint8, device=dev) if wl.requant else None
+        else:
+            self.out = torch.empty((self.m, self.n), dtype=torch.bfloat16, device=dev)
+        if wl.epilogue == "rmsnorm_head":
+            self.norm_w = torch.from_numpy(wl.norm_w).to(dev, torch.float32)
+        self.flops = 2 * self.m * self.n * self.k
+        self.ops = ops
+
+    def quantize(self, step):
+        x = self.xs[step % len(self.xs)]
+        if self.t is not None:
+            self.ops.block_transform(x, self.t, quantize=True, out=(None, self.a_codes, self.a_scales))
+        else:
+            self.ops.quantize_mxfp4(x, self.a_codes, self.a_scales)
+
+    def gemm(self):
+        ops, wl = self.ops, self.wl
+        if wl.epilogue == "rmsnorm_head":
+            ops.gemm_fp4_epilogue_rmsnorm_head(self.a_codes, self.a_scales, self.b_codes, self.b_scales,
+                                               wl.head_dim, wl.n_norm, self.norm_w, wl.eps, out=self.out)
+        elif wl.epilogue == "swiglu":
+            ops.gemm_fp4_epilogue_swiglu(self.a_codes, self.a_scales, self.b_codes, self.b_scales,
+                                         out_dtype=torch_bf16(), requant=wl.requant,
+                                         out=(self.out, self.codes, self.scales))
+        else:
+            ops.gemm_fp4_epilogue_none(self.a_codes, self.a_scales, self.b_codes, self.b_scales, out=self.out)
+
+    def quant_bytes(self):
+        """Algorithmic HBM bytes of the activation quantiser: bf16 in, codes + scales out."""
+        return self.m * self.k * 2 + self.m * self.k // 2 + self.m * self.k // 32
+
+    def gemm_bytes(self):
+        """Algorithmic HBM bytes of the fused GEMM: both MXFP4 operands once, output once."""
+        ab = self.m * self.k // 2 + self.m * self.k // 32
+        bb = self.n * self.k // 2 + self.n * self.k // 32
+        if self.wl.epilogue == "swiglu":
+            ob = self.m * (self.n // 4 + self.n // 64) if self.wl.requant else self.m * self.n
+        else:
+            ob = self.m * self.n * 2
+        return ab + bb + ob
+
+
+def torch_bf16():
+    import torch
+    return torch.bfloat16
+
+
+def build_layers(args, ops, torch, workloads):
+    if args.workload == "dit_1k_linears":
+        wls = [workloads.qkv_hd128(), workloads.qkv_hd256(), workloads.ffn_up_swiglu(requant=True)]
+        return [Layer(w.name, w, ops, torch, args.rotate) for w in wls]
+    qkv, up, down = workloads.dit_block()
+    layers = [Layer("dit_block_qkv", qkv, ops, torch, args.rotate, transform=qkv.t),
+              Layer("dit_block_up", up, ops, torch, args.rotate, transform=up.t)]
+    # The down projection's input is the up projection's bf16 SwiGLU output.
+    up_layer = layers[1]
+    up_layer.wl.requant = False
+    n_half = up_layer.n // 2
+    up_layer.out = torch.empty((up_layer.m, n_half), dtype=torch.bfloat16, device="cuda")
+    up_layer.codes = up_layer.scales = None
+    down.x = np.zeros((down.m, down.k), dtype=np.float32)          # placeholder: replaced below
+    dl = Layer("dit_block_down", down, ops, torch, 1, transform=down.t)
+    dl.xs = [up_layer.out]
+    layers.append(dl)
+    return layers
+
+
+# --------------------------------------------------------------- measuring --
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp4_diffusion_transformer_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILES, "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel_key)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(args, layers_wl, rows=2048):
+    """The oracle as it stands, on a bounded sample of the same workload: the
+    first `rows` tokens of every layer.  Timed: activation [transform +]
+    quantise, the dequantise-then-fp64 GEMM and the epilogue; weight
+    quantisation (offline on both sides) is outside the timed region."""
+    sys.path.insert(0, ROOT)
+    from oracle import gemm as ogemm
+    from oracle import mxfp4
+    from oracle import transform as otransform
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        threads = max(i.get("num_threads", 1) for i in info) if info else 1
+    except Exception:  # noqa: BLE001
+        threads = 1
+    flops, elapsed = 0, 0.0
+    for wl in layers_wl:
+        x = wl.x[:rows].astype(np.float64)
+        t = None if wl.t is None else wl.t.astype(np.float64)
+        if wl.epilogue == "swiglu":
+            wg, wu = wl.w_gate.astype(np.float64), wl.w_up.astype(np.float64)
+            if t is not None:
+                wg, wu = otransform.fold_inverse(wg, t), otransform.fold_inverse(wu, t)
+            gc_, gs_ = mxfp4.quantize(wg.T)
+            uc_, us_ = mxfp4.quantize(wu.T)
+            n = 2 * wl.w_gate.shape[1]
+        else:
+            w = wl.w.astype(np.float64)
+            if t is not None:
+                w = otransform.fold_inverse(w, t)
+            bc, bs = mxfp4.quantize(w.T)
+            n = wl.w.shape[1]
+        t1 = time.perf_counter()
+        ac, as_ = mxfp4.quantize(x) if t is None else otransform.transform_quantize(x, t)
+        if wl.epilogue == "swiglu":
+            h = ogemm.swiglu(ogemm.gemm(ac, as_, gc_, gs_), ogemm.gemm(ac, as_, uc_, us_))
+            if wl.requant:
+                ogemm.requantize(h)
+        else:
+            c = ogemm.gemm(ac, as_, bc, bs)
+            if wl.epilogue == "rmsnorm_head":
+                ogemm.rmsnorm_head(c, wl.head_dim, wl.n_norm, wl.norm_w.astype(np.float64), wl.eps)
+        elapsed += time.perf_counter() - t1
+        flops += 2 * rows * n * wl.k
+    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": "first %d tokens of each layer of the workload (%s); %.1f s timed" % (
+                rows, ", ".join(w.name for w in layers_wl), elapsed)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+              "(the path shards by tokens with no exchange, see DESIGN.md)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    sys.path.insert(0, ROOT)
+    from fp4_diffusion_transformer_amd import ops, workloads
+
+    torch.cuda.init()
+    layers = build_layers(args, ops, torch, workloads)
+    torch.cuda.synchronize()
+
+    # dominant kernel = the GEMM with the most flops in a step
+    dom = max(range(len(layers)), key=lambda i: layers[i].flops)
+    quant_dom = max(range(len(layers)), key=lambda i: layers[i].quant_bytes())
+
+    def step(s, ev=None):
+        for i, L in enumerate(layers):
+            if ev is not None and i == quant_dom:
+                ev["q0"][s].record()
+            L.quantize(s)
+            if ev is not None and i == quant_dom:
+                ev["q1"][s].record()
+            if ev is not None and i == dom:
+                ev["g0"][s].record()
+            L.gemm()
+            if ev is not None and i == dom:
+                ev["g1"][s].record()
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+
+    ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)] for k in ("g0", "g1", "q0", "q1")}
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        step(s, ev)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    flops = sum(L.flops for L in layers)
+    tflops = flops / (ms_step * 1e-3) / 1e12
+
+    g_ms = [ev["g0"][s].elapsed_time(ev["g1"][s]) for s in range(args.steps)]
+    q_ms = [ev["q0"][s].elapsed_time(ev["q1"][s]) for s in range(args.steps)]
+    g_avg = float(np.mean(g_ms))
+    q_avg = float(np.mean(q_ms))
+    Ld, Lq = layers[dom], layers[quant_dom]
+    achieved = Ld.flops / (g_avg * 1e-3) / 1e12
+    kernel_key = "gemm_" + Ld.wl.epilogue + ("_requant" if Ld.wl.requant else "")
+
+    out = {
+        "metric": "fused MXFP4 GEMM+epilogue TFLOPS and % of MXFP4 peak at DiT 1K shapes",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "layers": [{"name": L.name, "M": L.m, "N": L.n, "K": L.k, "epilogue": L.wl.epilogue
+                        + ("+requant" if L.wl.requant else "") + ("+transform" if L.t is not None else "")}
+                       for L in layers],
+            "pct_of_mxfp4_peak": round(100.0 * tflops / PEAK_MXFP4_TFLOPS, 2),
+            "wall_s_timed": round(wall, 3),
+        },
+        "roofline": {
+            "kernel": kernel_key + " (%s, M=%d N=%d K=%d)" % (Ld.name, Ld.m, Ld.n, Ld.k),
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_MXFP4_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_MXFP4_TFLOPS, 4),
+            "traffic": traffic_from_profile(kernel_key),
+            "avg_launch_ms": round(g_avg, 5),
+            "algorithmic_bytes": Ld.gemm_bytes(),
+        },
+        "quantize_roofline": {
+            "kernel": ("block_transform" if Lq.t is not None else "quantize_mxfp4") + " (%s, %dx%d bf16)"
+                      % (Lq.name, Lq.m, Lq.k),
+            "bound": "hbm",
+            "achieved": round(Lq.quant_bytes() / (q_avg * 1e-3) / 1e9, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(Lq.quant_bytes() / (q_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "avg_launch_ms": round(q_avg, 5),
+            "algorithmic_bytes": Lq.quant_bytes(),
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args, [L.wl for L in layers if L.wl.x is not None and
+                                                  L.name != "dit_block_down"])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
