@@ -7,42 +7,62 @@
 // extra HBM round trip.  KroQuant, "Deep analysis": both operands are MXFP4.
 //
 // Design (MI355X-first; the Blackwell tiling on the fal page is prior art):
-// * Contraction on V_MFMA_SCALE_F32_32X32X64_F8F6F4 with FP4 operands: it
-//   reaches the FP4 matrix rate, while the 16x16x128 shape only reaches half
-//   of it on this chip.  Its scale operand carries one e8m0 byte per lane,
-//   which is exactly one MX block (lane l holds row l%32, 32 K-elements).
-// * The GEMM is computed transposed, D = W . X^T: the weight rows (output
-//   channels) are the MFMA "A" operand and the tokens the "B" operand, so a
-//   lane's 16 accumulators of a 32x32 block are 4 runs of 4 consecutive
-//   channels of one token.  Per-head sums then need one cross-lane step
-//   (lane l and l^32) and stores are 8/16-byte vectors.
-// * Workgroup tile 256 channels x 256 tokens, 4 waves of 128 x 128 (256 fp32
-//   accumulators per lane), K staged 256 at a time through LDS, double
-//   buffered (2 x 68 KiB).  Global -> LDS uses the direct-to-LDS
-//   global_load_lds_dwordx4 (no VGPR staging); a row's 16-byte chunks are
-//   XOR-swizzled with the row index so the fragment reads (ds_read_b128,
-//   8 rows per 128 bytes) are free of bank conflicts.
-// * K is permuted inside a stage: in K-step s lane group h (= lane / 32)
-//   takes MX block 4h + s, so a lane's four scale bytes of a stage are
-//   adjacent, one ds_read_b32 fetches them and op_sel picks the byte.  Both
-//   operands use the same permutation, so the sum over K is unchanged.
+// * Contraction on V_MFMA_SCALE_F32_32X32X64_F8F6F4 with FP4 operands (the
+//   16x16x128 shape only reaches half the FP4 rate on this chip).  Its scale
+//   operand carries one e8m0 byte per lane, exactly one MX block: lane l
+//   holds row l%32 and the 32 K-elements of block l/32.
+// * The GEMM is computed transposed, D = W . X^T: weight rows (output
+//   channels) are the MFMA "A" operand, tokens the "B" operand, so a lane's
+//   16 accumulators of a 32x32 block are 4 runs of 4 consecutive channels of
+//   one token: a per-head sum needs one lane swap (l <-> l^32).
+// * Workgroup tile 256 channels x 128 tokens, 4 waves of 128 x 64 (128 fp32
+//   accumulators per lane).  With 76.5 KiB of LDS and <= 256 registers per
+//   lane two workgroups share a CU, so one workgroup's epilogue overlaps the
+//   other's main loop.
+// * K is staged 128 at a time through a 3-deep LDS ring filled by the
+//   direct-to-LDS global_load_lds_dwordx4 (no VGPR staging); stage kt+2 is in
+//   flight while stage kt is multiplied.  One barrier per stage.  The three
+//   ring slots are distinct __shared__ objects and the K loop is unrolled by
+//   three, so every LDS access names its slot statically: the compiler can
+//   then tell the fragment reads of stage kt+1 from the loads still landing
+//   in stage kt+2 and does not drain all loads before each read.
+// * LDS rows are 64 B (4 chunks of 16 B, one MX block each).  Chunk c of row
+//   r is stored at c ^ ((r >> 2) & 3): each quarter-wave of a fragment read
+//   (16 lanes = rows 0..15, 16 B each) then covers all 64 banks once.
+// * K is permuted inside a stage: in K-step s lane group h takes MX block
+//   2h + s, so a lane's two scale bytes of a stage are adjacent; one LDS
+//   read fetches them and op_sel picks the byte.  Both operands use
+//   the same permutation, so the sum over K is unchanged.
+// * bf16 outputs go through LDS (after the main loop) so that every global
+//   store writes whole row segments.
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace fp4dit {
 namespace {
 
-constexpr int kBM = 256;              // tokens per workgroup
-constexpr int kBN = 256;              // channels per workgroup
-constexpr int kBK = 256;              // K elements per LDS stage
-constexpr int kRowBytes = kBK / 2;    // 128 bytes of codes per row per stage
-constexpr int kScaleBytes = kBK / 32; // 8 scale bytes per row per stage
+constexpr int kBN = 256;               // channels per workgroup
+constexpr int kBM = 128;               // tokens per workgroup
+constexpr int kBK = 128;               // K elements per LDS stage
+constexpr int kStages = 3;
+constexpr int kRowBytes = kBK / 2;     // 64 bytes of codes per row per stage
+constexpr int kScaleBytes = kBK / 32;  // 4 scale bytes per row per stage
 constexpr int kWCodesOff = 0;
-constexpr int kXCodesOff = kWCodesOff + kBN * kRowBytes;        // 32 KiB
-constexpr int kWScalesOff = kXCodesOff + kBM * kRowBytes;       // 64 KiB
-constexpr int kXScalesOff = kWScalesOff + kBN * kScaleBytes;    // +2 KiB
-constexpr int kStageBytes = kXScalesOff + kBM * kScaleBytes;    // 68 KiB
-constexpr int kLdsBytes = 2 * kStageBytes;                      // 136 KiB
+constexpr int kXCodesOff = kWCodesOff + kBN * kRowBytes;        // 16 KiB
+constexpr int kWScalesOff = kXCodesOff + kBM * kRowBytes;       // +8 KiB
+constexpr int kXScalesOff = kWScalesOff + kBN * kScaleBytes;    // +1 KiB
+// Token scales: wave w loads rows 32w..32w+31 with all 64 lanes (lanes 32..63
+// repeat them), so each wave owns a 256-byte slot whose first half is used.
+constexpr int kStageBytes = kXScalesOff + 4 * 256;              // 26 KiB
+constexpr int kLdsBytes = kStages * kStageBytes;                // 78 KiB
+// Epilogue reuse of the ring: each wave stages 32 tokens x 256 B of bf16 at
+// a time (8 KiB): waves 0..2 in stages 0..2, wave 3 in the second 8 KiB of
+// stage 0; the per-token head sums (1 KiB) sit behind wave 1's region.
+constexpr int kStageOutBytes = 8192;
+constexpr int kRedOff = kStageOutBytes;
+static_assert(2 * kStageOutBytes <= kStageBytes && kRedOff + 2 * kBM * 4 <= kStageBytes,
+              "epilogue LDS does not fit");
+constexpr int kDmaPerStage = 8;        // direct-to-LDS instructions per wave per stage
 
 enum EpiKind { kEpiNone = 0, kEpiRmsNorm = 1, kEpiSwiglu = 2 };
 
@@ -53,7 +73,6 @@ struct GemmArgs {
     const uint8_t* b_codes;
     const uint8_t* b_scales;
     void* out;
-    int out_bf16;
     // rmsnorm
     int head_dim;
     int64_t n_norm;
@@ -66,90 +85,114 @@ struct GemmArgs {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Per-lane state of the direct-to-LDS loads: 32-bit byte offsets from the
-// operand base, fixed for the whole K loop (the K stage advances the
-// wave-uniform base instead, so the loads use the SGPR-base addressing form).
+// s_waitcnt immediate (gfx9 encoding): vmcnt, expcnt, lgkmcnt.
+constexpr int waitcnt_imm(int vm, int exp, int lgkm) {
+    return (vm & 15) | ((exp & 7) << 4) | ((lgkm & 15) << 8) | (((vm >> 4) & 3) << 14);
+}
+
+// Workgroup barrier of the K loop.  __syncthreads() would add a release
+// fence, which drains every outstanding load -- including the direct-to-LDS
+// loads of stage kt+2 that are meant to stay in flight.  Instead each wave
+// waits explicitly (its stage-kt+1 loads landed: at most VM loads remain;
+// its own LDS reads done) and then meets the others at s_barrier.  The empty
+// asm statements keep the compiler from moving LDS accesses across it.
+template <int VM>
+__device__ __forceinline__ void ring_barrier() {
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(VM, 7, 0));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Per-lane byte offsets of the direct-to-LDS loads, fixed for the K loop (the
+// stage advances the wave-uniform base pointers instead).
 struct LoadPlan {
-    uint32_t w_code[8], x_code[8];    // 8 groups of 8 rows x 128 B per operand
-    uint32_t w_scale[2], x_scale[2];  // 2 groups of 32 rows x 8 B per operand
+    uint32_t w_code[4], x_code[2];
+    uint32_t w_scale, x_scale;
 };
 
 __device__ __forceinline__ LoadPlan make_plan(const GemmArgs& g, int64_t n0, int64_t m0, int wave, int lane) {
     LoadPlan p;
     const uint32_t kcb = (uint32_t)(g.K / 2);
     const uint32_t ksb = (uint32_t)(g.K / 32);
-    const int rin = lane >> 3;             // row within an 8-row group
-    const int lchunk = (lane & 7) ^ rin;   // logical chunk written to physical chunk lane & 7
+    const int rin = lane >> 2;                          // row within a 16-row group
+    const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);  // chunk for physical slot lane & 3
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int row = (wave * 8 + j) * 8 + rin;
-        int64_t xr = m0 + row;
-        xr = xr < g.M ? xr : g.M - 1;     // ragged token tile: clamp, never stored
+    for (int j = 0; j < 4; ++j) {
+        const int row = (wave * 4 + j) * 16 + rin;
         p.w_code[j] = (uint32_t)(n0 + row) * kcb + lchunk * 16;
-        p.x_code[j] = (uint32_t)xr * kcb + lchunk * 16;
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int row = (wave * 2 + j) * 32 + (lane >> 1);
+        const int row = (wave * 2 + j) * 16 + rin;
         int64_t xr = m0 + row;
-        xr = xr < g.M ? xr : g.M - 1;
-        p.w_scale[j] = (uint32_t)(n0 + row) * ksb + (lane & 1) * 4;
-        p.x_scale[j] = (uint32_t)xr * ksb + (lane & 1) * 4;
+        xr = xr < g.M ? xr : g.M - 1;                   // ragged token tile: clamp, never stored
+        p.x_code[j] = (uint32_t)xr * kcb + lchunk * 16;
     }
+    p.w_scale = (uint32_t)(n0 + wave * 64 + lane) * ksb;
+    int64_t xr = m0 + wave * 32 + (lane & 31);          // lanes 32..63 repeat lanes 0..31
+    xr = xr < g.M ? xr : g.M - 1;
+    p.x_scale = (uint32_t)xr * ksb;
     return p;
 }
 
-// Enqueue the direct-to-LDS loads of K stage kt into `stage`.
-__device__ __forceinline__ void issue_stage(uint8_t* stage, const GemmArgs& g, const LoadPlan& p,
-                                            int kt, int wave) {
+// Enqueue the 8 direct-to-LDS loads of K stage kt into `stage` (this wave's share).
+__device__ __forceinline__ void issue_stage(uint8_t* stage, const GemmArgs& g, const LoadPlan& p, int kt,
+                                            int wave, int lane) {
     const uint8_t* wc = g.b_codes + (int64_t)kt * kRowBytes;
     const uint8_t* xc = g.a_codes + (int64_t)kt * kRowBytes;
-    const uint8_t* ws = g.b_scales + (int64_t)kt * kScaleBytes;
-    const uint8_t* xs = g.a_scales + (int64_t)kt * kScaleBytes;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int grp = wave * 8 + j;
-        __builtin_amdgcn_global_load_lds(wc + p.w_code[j], (lds_void*)(stage + kWCodesOff + grp * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(xc + p.x_code[j], (lds_void*)(stage + kXCodesOff + grp * 1024), 16, 0, 0);
-    }
+    for (int j = 0; j < 4; ++j)
+        __builtin_amdgcn_global_load_lds(wc + p.w_code[j], (lds_void*)(stage + kWCodesOff + (wave * 4 + j) * 1024),
+                                         16, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int grp = wave * 2 + j;
-        __builtin_amdgcn_global_load_lds(ws + p.w_scale[j], (lds_void*)(stage + kWScalesOff + grp * 256), 4, 0, 0);
-        __builtin_amdgcn_global_load_lds(xs + p.x_scale[j], (lds_void*)(stage + kXScalesOff + grp * 256), 4, 0, 0);
-    }
+    for (int j = 0; j < 2; ++j)
+        __builtin_amdgcn_global_load_lds(xc + p.x_code[j], (lds_void*)(stage + kXCodesOff + (wave * 2 + j) * 1024),
+                                         16, 0, 0);
+    __builtin_amdgcn_global_load_lds(g.b_scales + (int64_t)kt * kScaleBytes + p.w_scale,
+                                     (lds_void*)(stage + kWScalesOff + wave * 256), 4, 0, 0);
+    // 128 token rows of scales: 32 per wave, into the wave's 256-byte slot
+    __builtin_amdgcn_global_load_lds(g.a_scales + (int64_t)kt * kScaleBytes + p.x_scale,
+                                     (lds_void*)(stage + kXScalesOff + wave * 256), 4, 0, 0);
 }
 
 struct Frags {
-    v4i w[4], x[4];
+    v4i w[4], x[2];
 };
 
-// Fragment reads of K-step s: lane group h takes MX block 4h + s of the stage.
+// Fragment reads of K-step s: lane group h takes MX block 2h + s of the stage.
 __device__ __forceinline__ void read_frags(Frags& f, const uint8_t* stage, int wn, int wm, int r32, int h,
-                                           int swz, int s) {
-    const int chunk = ((4 * h + s) ^ swz) * 16;
+                                           int s) {
+    const int chunk = ((2 * h + s) ^ ((r32 >> 2) & 3)) * 16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i)
         f.w[i] = *reinterpret_cast<const v4i*>(stage + kWCodesOff + (wn * 128 + i * 32 + r32) * kRowBytes + chunk);
-        f.x[i] = *reinterpret_cast<const v4i*>(stage + kXCodesOff + (wm * 128 + i * 32 + r32) * kRowBytes + chunk);
-    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        f.x[i] = *reinterpret_cast<const v4i*>(stage + kXCodesOff + (wm * 64 + i * 32 + r32) * kRowBytes + chunk);
 }
 
+// Scale bytes 2h, 2h+1 of every fragment row (byte s serves K-step s),
+// read as the row's whole dword: a 16-bit LDS read here makes the compiler
+// wait for every load still in flight (it cannot tell it apart from the
+// loads landing in the other ring slots), a 32-bit one does not.
 __device__ __forceinline__ void read_scales(uint32_t* wsc, uint32_t* xsc, const uint8_t* stage, int wn, int wm,
                                             int r32, int h) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        wsc[i] = *reinterpret_cast<const uint32_t*>(stage + kWScalesOff + (wn * 128 + i * 32 + r32) * kScaleBytes + h * 4);
-        xsc[i] = *reinterpret_cast<const uint32_t*>(stage + kXScalesOff + (wm * 128 + i * 32 + r32) * kScaleBytes + h * 4);
-    }
+    for (int i = 0; i < 4; ++i)
+        wsc[i] = *reinterpret_cast<const uint32_t*>(stage + kWScalesOff + (wn * 128 + i * 32 + r32) * kScaleBytes) >> (16 * h);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)   // token row wm*64 + i*32 + r32 sits in slot (2wm + i) at r32*4
+        xsc[i] = *reinterpret_cast<const uint32_t*>(stage + kXScalesOff + (wm * 2 + i) * 256 + r32 * kScaleBytes) >> (16 * h);
 }
 
 template <int S>
-__device__ __forceinline__ void mfma_step(v16f (&acc)[4][4], const Frags& f, const uint32_t* wsc, const uint32_t* xsc) {
+__device__ __forceinline__ void mfma_step(v16f (&acc)[4][2], const Frags& f, const uint32_t* wsc,
+                                          const uint32_t* xsc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 2; ++j) {
             const v8i a = {f.w[i][0], f.w[i][1], f.w[i][2], f.w[i][3], 0, 0, 0, 0};
             const v8i b = {f.x[j][0], f.x[j][1], f.x[j][2], f.x[j][3], 0, 0, 0, 0};
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 4, 4, S, (int)wsc[i],
@@ -157,39 +200,28 @@ __device__ __forceinline__ void mfma_step(v16f (&acc)[4][4], const Frags& f, con
         }
 }
 
-// Scheduling of one K-step: its 16 MFMAs interleaved with the 8 fragment
-// reads of the next K-step (one read, then two MFMAs), and in the first step
-// of a stage also with the 20 direct-to-LDS loads of the following stage.
-// Masks: 0x008 MFMA, 0x010 VMEM, 0x100 DS read.
-__device__ __forceinline__ void interleave_reads_mfma() {
+// Scheduling of one K-step: its 8 MFMAs interleaved with the 6 fragment
+// reads of the next K-step and, in the first K-step of a stage, with the 8
+// direct-to-LDS loads of stage kt+2 (masks: 0x008 MFMA, 0x020 VMEM read,
+// 0x100 DS read).
+__device__ __forceinline__ void sched_step0() {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 6; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
 }
-__device__ __forceinline__ void interleave_loads_reads_mfma() {
+__device__ __forceinline__ void sched_step1() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x010, 3, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-}
-__device__ __forceinline__ void interleave_scales_reads_mfma() {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 6; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -197,13 +229,13 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)
 
 // Map the linear workgroup id to a (token tile, channel tile).  Workgroups
 // are dispatched round-robin over the 8 XCDs; consecutive remapped ids land
-// on one XCD and walk a band of 4 token tiles across the channel tiles, so
+// on one XCD and walk a band of 8 token tiles across the channel tiles, so
 // the workgroups an XCD runs together share operand rows in its L2.
 __device__ __forceinline__ void tile_of(int64_t bid, int64_t nwg, int64_t tiles_n, int64_t tiles_m,
                                         int64_t& tm, int64_t& tn) {
     int64_t b = bid;
     if ((nwg & 7) == 0) b = (bid & 7) * (nwg >> 3) + (bid >> 3);
-    constexpr int64_t kGroupM = 4;
+    constexpr int64_t kGroupM = 8;
     const int64_t per_group = kGroupM * tiles_n;
     const int64_t group = b / per_group;
     const int64_t first = group * kGroupM;
@@ -213,101 +245,148 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t nwg, int64_t tiles_
     tn = in / gm;
 }
 
-template <int EPI, bool OUT_BF16>
-__global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
+// Store 32 tokens x 8Q bf16 columns of this wave through its LDS region so
+// that every global store writes whole row segments.  vals(q, v) gives the
+// lane's 4 fp32 values of 8-column chunk q (half h) for token tok0 + r32.
+// In LDS, chunk q of token row t sits at q ^ (t % Q) and its two halves are
+// swapped on every other group of Q rows, so both the 8-byte writes and the
+// 16-byte row reads spread over all banks.  Called by all 4 waves together.
+template <int Q, typename F>
+__device__ __forceinline__ void store_bf16_half(uint8_t* region, F vals, uint16_t* out, int64_t ld,
+                                                int64_t tok0, int64_t col0, int64_t M, int r32, int h, int lane) {
+    constexpr int kRow = Q * 16;                       // bytes per token row
+    const int t = r32;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        float v[4];
+        vals(q, v);
+        v2u o;
+        o[0] = pack_bf16x2(v[0], v[1]);
+        o[1] = pack_bf16x2(v[2], v[3]);
+        const int off = t * kRow + ((q ^ (t % Q)) * 16) + ((h ^ ((t / Q) & 1)) * 8);
+        *reinterpret_cast<v2u*>(region + off) = o;
+    }
+    __syncthreads();
+    constexpr int kRowsPerInst = 64 / Q;               // Q lanes x 16 B per token row
+#pragma unroll
+    for (int it = 0; it < 32 / kRowsPerInst; ++it) {
+        const int tr = it * kRowsPerInst + lane / Q;
+        const int q = lane % Q;
+        v4u v = *reinterpret_cast<const v4u*>(region + tr * kRow + ((q ^ (tr % Q)) * 16));
+        if ((tr / Q) & 1) v = (v4u){v[2], v[3], v[0], v[1]};
+        const int64_t tok = tok0 + tr;
+        if (tok < M) *reinterpret_cast<v4u*>(out + tok * ld + col0 + q * 8) = v;
+    }
+    __syncthreads();
+}
+
+// One K stage of the main loop on ring slot `cur` (static).  ISSUE: also
+// enqueue the loads of stage kt+2 into slot `fill`; NEXT: prefetch the scales
+// and first fragments of stage kt+1 from slot `nxt` after the barrier.
+template <bool ISSUE, bool NEXT>
+__device__ __forceinline__ void k_stage(v16f (&acc)[4][2], Frags& f0, Frags& f1, uint32_t* wsc, uint32_t* xsc,
+                                        uint8_t* cur, uint8_t* nxt, uint8_t* fill, const GemmArgs& g,
+                                        const LoadPlan& plan, int kt, int wave, int lane, int wn, int wm, int r32,
+                                        int h) {
+    uint32_t wsn[4], xsn[2];
+    if (ISSUE) issue_stage(fill, g, plan, kt + 2, wave, lane);
+    read_frags(f1, cur, wn, wm, r32, h, 1);
+    mfma_step<0>(acc, f0, wsc, xsc);
+    if (ISSUE) sched_step0(); else sched_step1();
+    if (NEXT) {
+        // Stage kt+1 landed (only stage kt+2's loads may remain) and this
+        // stage's fragments are in registers: after the barrier stage kt+1
+        // may be read and stage kt overwritten.
+        ring_barrier<ISSUE ? kDmaPerStage : 0>();
+        read_scales(wsn, xsn, nxt, wn, wm, r32, h);
+        read_frags(f0, nxt, wn, wm, r32, h, 0);
+    }
+    mfma_step<1>(acc, f1, wsc, xsc);
+    if (NEXT) {
+        sched_step1();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wsc[i] = wsn[i];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) xsc[i] = xsn[i];
+    }
+}
+
+template <int EPI, bool OUT_BF16, int REM>
+__global__ __launch_bounds__(256, 2) void gemm_fp4_kernel(GemmArgs g) {
+    __shared__ __attribute__((aligned(1024))) uint8_t ring0[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring1[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring2[kStageBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wn = wave & 1;              // channel half of the workgroup tile
-    const int wm = wave >> 1;             // token half
+    const int wn = wave & 1;              // channel half of the workgroup tile (128 channels)
+    const int wm = wave >> 1;             // token half (64 tokens)
     const int64_t tiles_n = g.N / kBN;
     const int64_t tiles_m = (g.M + kBM - 1) / kBM;
     int64_t tm, tn;
     tile_of(blockIdx.x, (int64_t)gridDim.x, tiles_n, tiles_m, tm, tn);
     const int64_t n0 = tn * kBN;
     const int64_t m0 = tm * kBM;
-    const int kt_count = (int)(g.K / kBK);
+    const int kt_count = (int)(g.K / kBK);   // even and >= 2 (K % 256 == 0)
 
-    v16f acc[4][4];
+    v16f acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = (v16f){};
+        for (int j = 0; j < 2; ++j) acc[i][j] = (v16f){};
 
     const int r32 = lane & 31;
     const int h = lane >> 5;
-    const int swz = lane & 7;             // row & 7 of every fragment row this lane reads
 
+    // Ring slot of stage j is (j + OFF) % 3 with OFF chosen so that the
+    // REM = (kt_count - 2) % 3 stages before the unrolled loop absorb the
+    // remainder: the loop then always starts on slot 0 and the last two
+    // stages always sit in slots 0 and 1, all known at compile time.
+    constexpr int OFF = (3 - REM) % 3;
+    uint8_t* const slots[3] = {ring0, ring1, ring2};
     const LoadPlan plan = make_plan(g, n0, m0, wave, lane);
-    issue_stage(smem, g, plan, 0, wave);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    issue_stage(slots[OFF % 3], g, plan, 0, wave, lane);
+    issue_stage(slots[(OFF + 1) % 3], g, plan, 1, wave, lane);
+    ring_barrier<kDmaPerStage>();                    // stage 0 landed
 
     Frags f0, f1;
-    uint32_t wsc[4], xsc[4], wsn[4], xsn[4];
-    read_scales(wsc, xsc, smem, wn, wm, r32, h);
-    read_frags(f0, smem, wn, wm, r32, h, swz, 0);
+    uint32_t wsc[4], xsc[2];
+    read_scales(wsc, xsc, slots[OFF % 3], wn, wm, r32, h);
+    read_frags(f0, slots[OFF % 3], wn, wm, r32, h, 0);
 
-    // Steady state: stage kt is computed while stage kt+1 streams in.  The
-    // loop body has no branches (the last stage is peeled below) so the
-    // compiler keeps the MFMAs interleaved with the fragment reads.
-    for (int kt = 0; kt < kt_count - 1; ++kt) {
-        const uint8_t* cur = smem + (kt & 1) * kStageBytes;
-        uint8_t* nxt = smem + ((kt + 1) & 1) * kStageBytes;
-        issue_stage(nxt, g, plan, kt + 1, wave);
-        read_frags(f1, cur, wn, wm, r32, h, swz, 1);
-        mfma_step<0>(acc, f0, wsc, xsc);
-        interleave_loads_reads_mfma();
-        read_frags(f0, cur, wn, wm, r32, h, swz, 2);
-        mfma_step<1>(acc, f1, wsc, xsc);
-        interleave_reads_mfma();
-        read_frags(f1, cur, wn, wm, r32, h, swz, 3);
-        mfma_step<2>(acc, f0, wsc, xsc);
-        interleave_reads_mfma();
-        // Every wave has its stage-kt fragments in registers and its
-        // stage-kt+1 loads landed: after this barrier the next stage may be
-        // read and this one overwritten.
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        read_scales(wsn, xsn, nxt, wn, wm, r32, h);
-        read_frags(f0, nxt, wn, wm, r32, h, swz, 0);
-        mfma_step<3>(acc, f1, wsc, xsc);
-        interleave_scales_reads_mfma();
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            wsc[i] = wsn[i];
-            xsc[i] = xsn[i];
-        }
+#define FP4DIT_STAGE(ISSUE, NEXT, CUR, NXT, FILL, KT) \
+    k_stage<ISSUE, NEXT>(acc, f0, f1, wsc, xsc, slots[CUR], slots[NXT], slots[FILL], g, plan, KT, wave, lane, \
+                         wn, wm, r32, h)
+    // stages 0 .. REM-1 (each issues the loads of stage j + 2)
+    if (REM >= 1) FP4DIT_STAGE(true, true, (OFF + 0) % 3, (OFF + 1) % 3, (OFF + 2) % 3, 0);
+    if (REM >= 2) FP4DIT_STAGE(true, true, (OFF + 1) % 3, (OFF + 2) % 3, (OFF + 0) % 3, 1);
+    // stages REM .. kt_count - 3, three at a time, on slots 0, 1, 2
+    for (int kt = REM; kt < kt_count - 2; kt += 3) {
+        FP4DIT_STAGE(true, true, 0, 1, 2, kt);
+        FP4DIT_STAGE(true, true, 1, 2, 0, kt + 1);
+        FP4DIT_STAGE(true, true, 2, 0, 1, kt + 2);
     }
-    {
-        const uint8_t* cur = smem + ((kt_count - 1) & 1) * kStageBytes;
-        read_frags(f1, cur, wn, wm, r32, h, swz, 1);
-        mfma_step<0>(acc, f0, wsc, xsc);
-        interleave_reads_mfma();
-        read_frags(f0, cur, wn, wm, r32, h, swz, 2);
-        mfma_step<1>(acc, f1, wsc, xsc);
-        interleave_reads_mfma();
-        read_frags(f1, cur, wn, wm, r32, h, swz, 3);
-        mfma_step<2>(acc, f0, wsc, xsc);
-        interleave_reads_mfma();
-        mfma_step<3>(acc, f1, wsc, xsc);
-    }
-    __syncthreads();                      // the epilogue may reuse the LDS
+    // the last two stages: no more loads
+    FP4DIT_STAGE(false, true, 0, 1, 2, kt_count - 2);
+    FP4DIT_STAGE(false, false, 1, 2, 0, kt_count - 1);
+#undef FP4DIT_STAGE
+    __syncthreads();                      // the epilogue reuses the LDS ring
 
     // ------------------------------------------------------------ epilogue --
     // acc[nb][mb][i]: channel n0 + wn*128 + nb*32 + 8*(i/4) + 4h + i%4,
-    //                 token   m0 + wm*128 + mb*32 + r32.
+    //                 token   m0 + wm*64 + mb*32 + r32.
     const int64_t cbase = n0 + wn * 128;
+    const int64_t tok0 = m0 + wm * 64;
+    uint8_t* region = wave == 0 ? ring0 : wave == 1 ? ring1 : wave == 2 ? ring2 : ring0 + kStageOutBytes;
     if (EPI == kEpiNone || EPI == kEpiRmsNorm) {
-        float rstd[4] = {1.f, 1.f, 1.f, 1.f};
+        float rstd[2] = {1.f, 1.f};
         bool norm = false;
         if (EPI == kEpiRmsNorm) {
-            float* red = reinterpret_cast<float*>(smem);  // [2 wn][256 tokens]
-            float ss[4];
+            float* red = reinterpret_cast<float*>(ring1 + kRedOff);  // [2 wn][128 tokens]
+            float ss[2];
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
+            for (int mb = 0; mb < 2; ++mb) {
                 float s = 0.f;
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb)
@@ -318,96 +397,108 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
             if (g.head_dim == 256) {                      // head = both channel halves
                 if (h == 0) {
 #pragma unroll
-                    for (int mb = 0; mb < 4; ++mb) red[wn * 256 + wm * 128 + mb * 32 + r32] = ss[mb];
+                    for (int mb = 0; mb < 2; ++mb) red[wn * kBM + wm * 64 + mb * 32 + r32] = ss[mb];
                 }
                 __syncthreads();
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb) ss[mb] += red[(1 - wn) * 256 + wm * 128 + mb * 32 + r32];
+                for (int mb = 0; mb < 2; ++mb) ss[mb] += red[(1 - wn) * kBM + wm * 64 + mb * 32 + r32];
             }
             const int64_t head0 = g.head_dim == 256 ? n0 : cbase;
             norm = head0 < g.n_norm;
             const float inv_d = 1.0f / (float)g.head_dim;
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) rstd[mb] = rsqrtf(ss[mb] * inv_d + g.eps);
+            for (int mb = 0; mb < 2; ++mb) rstd[mb] = rsqrtf(ss[mb] * inv_d + g.eps);
         }
+        v4f wv[4][4];
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                const int64_t ch = cbase + nb * 32 + 8 * a + 4 * h;
-                v4f wv = {1.f, 1.f, 1.f, 1.f};
-                if (EPI == kEpiRmsNorm && norm) wv = *reinterpret_cast<const v4f*>(g.norm_w + ch);
+                wv[nb][a] = (v4f){1.f, 1.f, 1.f, 1.f};
+                if (EPI == kEpiRmsNorm && norm)
+                    wv[nb][a] = *reinterpret_cast<const v4f*>(g.norm_w + cbase + nb * 32 + 8 * a + 4 * h);
+            }
+        auto vals = [&](int q, int mb, float* v) {
+            const int nb = q >> 2, a = q & 3;
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb) {
-                    const int64_t tok = m0 + wm * 128 + mb * 32 + r32;
-                    if (tok >= g.M) continue;
-                    const v16f& c = acc[nb][mb];
+            for (int r = 0; r < 4; ++r)
+                v[r] = (EPI == kEpiRmsNorm && norm) ? acc[nb][mb][4 * a + r] * rstd[mb] * wv[nb][a][r]
+                                                    : acc[nb][mb][4 * a + r];
+        };
+        if (OUT_BF16) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+                store_bf16_half<16>(region, [&](int q, float* v) { vals(q, mb, v); }, static_cast<uint16_t*>(g.out),
+                                    g.N, tok0 + mb * 32, cbase, g.M, r32, h, lane);
+        } else {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                const int64_t tok = tok0 + mb * 32 + r32;
+                if (tok >= g.M) continue;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
                     float v[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        v[r] = (EPI == kEpiRmsNorm && norm) ? c[4 * a + r] * rstd[mb] * wv[r] : c[4 * a + r];
-                    if (OUT_BF16) {
-                        v2u o;
-                        o[0] = pack_bf16x2(v[0], v[1]);
-                        o[1] = pack_bf16x2(v[2], v[3]);
-                        *reinterpret_cast<v2u*>(static_cast<uint16_t*>(g.out) + tok * g.N + ch) = o;
-                    } else {
-                        *reinterpret_cast<v4f*>(static_cast<float*>(g.out) + tok * g.N + ch) =
-                            (v4f){v[0], v[1], v[2], v[3]};
-                    }
+                    vals(q, mb, v);
+                    *reinterpret_cast<v4f*>(static_cast<float*>(g.out) + tok * g.N + cbase + (q >> 2) * 32 +
+                                            8 * (q & 3) + 4 * h) = (v4f){v[0], v[1], v[2], v[3]};
                 }
             }
+        }
     }
 
     if (EPI == kEpiSwiglu) {
-        // Channel blocks alternate gate / up (interleave group 32): block
-        // 2q holds gate outputs and block 2q+1 the matching up outputs
-        // cbase/2 + 32q + 8a + 4h + r.
+        // Channel blocks alternate gate / up (interleave group 32): block 2p
+        // of the wave holds gate outputs and block 2p+1 the matching up
+        // outputs cbase/2 + 32p + 8a + 4h + r.
         const int64_t nh = g.N / 2;
+        const int64_t ob0 = cbase / 2;
+        float hv[2][2][16];                   // [p][mb][4a + r]
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            const int64_t tok = m0 + wm * 128 + mb * 32 + r32;
-            const bool live = tok < g.M;
+        for (int p = 0; p < 2; ++p)
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                float hv[16];
+            for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) hv[i] = silu_f(acc[2 * q][mb][i]) * acc[2 * q + 1][mb][i];
-                const int64_t ob = cbase / 2 + 32 * q;   // first output of this 32-block
-                if (g.out != nullptr && live) {
+                for (int i = 0; i < 16; ++i) hv[p][mb][i] = silu_f(acc[2 * p][mb][i]) * acc[2 * p + 1][mb][i];
+        if (g.out != nullptr) {
+            if (OUT_BF16) {
 #pragma unroll
-                    for (int a = 0; a < 4; ++a) {
-                        const int64_t oc = ob + 8 * a + 4 * h;
-                        if (OUT_BF16) {
-                            v2u v;
-                            v[0] = pack_bf16x2(hv[4 * a + 0], hv[4 * a + 1]);
-                            v[1] = pack_bf16x2(hv[4 * a + 2], hv[4 * a + 3]);
-                            *reinterpret_cast<v2u*>(static_cast<uint16_t*>(g.out) + tok * nh + oc) = v;
-                        } else {
-                            const v4f v = {hv[4 * a + 0], hv[4 * a + 1], hv[4 * a + 2], hv[4 * a + 3]};
-                            *reinterpret_cast<v4f*>(static_cast<float*>(g.out) + tok * nh + oc) = v;
-                        }
-                    }
+                for (int mb = 0; mb < 2; ++mb)
+                    store_bf16_half<8>(region, [&](int q, float* v) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) v[r] = hv[q >> 2][mb][4 * (q & 3) + r];
+                    }, static_cast<uint16_t*>(g.out), nh, tok0 + mb * 32, ob0, g.M, r32, h, lane);
+            } else {
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) {
+                    const int64_t tok = tok0 + mb * 32 + r32;
+                    if (tok >= g.M) continue;
+#pragma unroll
+                    for (int p = 0; p < 2; ++p)
+#pragma unroll
+                        for (int a = 0; a < 4; ++a)
+                            *reinterpret_cast<v4f*>(static_cast<float*>(g.out) + tok * nh + ob0 + 32 * p + 8 * a +
+                                                    4 * h) =
+                                (v4f){hv[p][mb][4 * a], hv[p][mb][4 * a + 1], hv[p][mb][4 * a + 2], hv[p][mb][4 * a + 3]};
                 }
-                if (g.out_codes != nullptr) {
-                    uint32_t hb[16];
+            }
+        }
+        if (g.out_codes != nullptr) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                const int64_t tok = tok0 + mb * 32 + r32;
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
                     uint32_t amax = 0u;
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        hb[i] = __float_as_uint(hv[i]);
-                        const uint32_t a = hb[i] & 0x7FFFFFFFu;
+                        const uint32_t a = __float_as_uint(hv[p][mb][i]) & 0x7FFFFFFFu;
                         amax = a > amax ? a : amax;
                     }
                     amax = max_xor32_u(amax);
                     const uint32_t sc = e8m0_from_amax_bits(amax);
                     uint32_t c16[4];                  // codes of outputs 8a+4h .. +3
 #pragma unroll
-                    for (int a = 0; a < 4; ++a) {
-                        uint32_t w = 0u;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) w |= e2m1_code(hb[4 * a + r], sc) << (4 * r);
-                        c16[a] = sc == 0xFFu ? 0u : w;
-                    }
+                    for (int a = 0; a < 4; ++a) c16[a] = sc == 0xFFu ? 0u : e2m1_pack4(&hv[p][mb][4 * a], sc);
                     // lane h=0 stores bytes 0..7 of the block (outputs 0..15),
                     // lane h=1 bytes 8..15; each needs two halves from its partner.
                     const uint32_t send = h == 0 ? (c16[2] | (c16[3] << 16)) : (c16[0] | (c16[1] << 16));
@@ -420,8 +511,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
                         st[0] = (recv & 0xFFFFu) | (c16[2] << 16);
                         st[1] = (recv >> 16) | (c16[3] << 16);
                     }
-                    if (live) {
-                        const int64_t blk = ob / 32;
+                    if (tok < g.M) {
+                        const int64_t blk = ob0 / 32 + p;
                         *reinterpret_cast<v2u*>(g.out_codes + tok * (nh / 2) + blk * 16 + h * 8) = st;
                         if (h == 0) g.out_scales[tok * (nh / 32) + blk] = (uint8_t)sc;
                     }
@@ -431,22 +522,31 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
     }
 }
 
-template <int EPI>
-void launch_epi(const GemmArgs& g, dim3 grid, hipStream_t stream) {
-    if (g.out_bf16) {
-        hipLaunchKernelGGL((gemm_fp4_kernel<EPI, true>), grid, dim3(256), 0, stream, g);
-    } else {
-        hipLaunchKernelGGL((gemm_fp4_kernel<EPI, false>), grid, dim3(256), 0, stream, g);
+template <int EPI, bool OUT_BF16>
+void launch_rem(const GemmArgs& g, dim3 grid, hipStream_t stream) {
+    switch ((g.K / kBK - 2) % 3) {
+        case 0: hipLaunchKernelGGL((gemm_fp4_kernel<EPI, OUT_BF16, 0>), grid, dim3(256), 0, stream, g); break;
+        case 1: hipLaunchKernelGGL((gemm_fp4_kernel<EPI, OUT_BF16, 1>), grid, dim3(256), 0, stream, g); break;
+        default: hipLaunchKernelGGL((gemm_fp4_kernel<EPI, OUT_BF16, 2>), grid, dim3(256), 0, stream, g); break;
     }
 }
 
-hipError_t launch_gemm(const GemmArgs& g, int epi, hipStream_t stream) {
+template <int EPI>
+void launch_epi(const GemmArgs& g, bool out_bf16, dim3 grid, hipStream_t stream) {
+    if (out_bf16) {
+        launch_rem<EPI, true>(g, grid, stream);
+    } else {
+        launch_rem<EPI, false>(g, grid, stream);
+    }
+}
+
+hipError_t launch_gemm(const GemmArgs& g, int epi, bool out_bf16, hipStream_t stream) {
     const int64_t tiles = (g.N / kBN) * ((g.M + kBM - 1) / kBM);
     const dim3 grid((unsigned)tiles);
     switch (epi) {
-        case kEpiNone: launch_epi<kEpiNone>(g, grid, stream); break;
-        case kEpiRmsNorm: launch_epi<kEpiRmsNorm>(g, grid, stream); break;
-        default: launch_epi<kEpiSwiglu>(g, grid, stream); break;
+        case kEpiNone: launch_epi<kEpiNone>(g, out_bf16, grid, stream); break;
+        case kEpiRmsNorm: launch_epi<kEpiRmsNorm>(g, out_bf16, grid, stream); break;
+        default: launch_epi<kEpiSwiglu>(g, out_bf16, grid, stream); break;
     }
     return hipGetLastError();
 }
@@ -459,8 +559,8 @@ hipError_t launch_gemm_none(int64_t M, int64_t N, int64_t K, const uint8_t* ac, 
     GemmArgs g{};
     g.M = M; g.N = N; g.K = K;
     g.a_codes = ac; g.a_scales = as; g.b_codes = bc; g.b_scales = bs;
-    g.out = out; g.out_bf16 = out_bf16 ? 1 : 0;
-    return launch_gemm(g, kEpiNone, stream);
+    g.out = out;
+    return launch_gemm(g, kEpiNone, out_bf16, stream);
 }
 
 hipError_t launch_gemm_rmsnorm(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
@@ -470,9 +570,9 @@ hipError_t launch_gemm_rmsnorm(int64_t M, int64_t N, int64_t K, const uint8_t* a
     GemmArgs g{};
     g.M = M; g.N = N; g.K = K;
     g.a_codes = ac; g.a_scales = as; g.b_codes = bc; g.b_scales = bs;
-    g.out = out; g.out_bf16 = out_bf16 ? 1 : 0;
+    g.out = out;
     g.head_dim = head_dim; g.n_norm = n_norm; g.norm_w = norm_w; g.eps = eps;
-    return launch_gemm(g, kEpiRmsNorm, stream);
+    return launch_gemm(g, kEpiRmsNorm, out_bf16, stream);
 }
 
 hipError_t launch_gemm_swiglu(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
@@ -481,9 +581,9 @@ hipError_t launch_gemm_swiglu(int64_t M, int64_t N, int64_t K, const uint8_t* ac
     GemmArgs g{};
     g.M = M; g.N = N; g.K = K;
     g.a_codes = ac; g.a_scales = as; g.b_codes = bc; g.b_scales = bs;
-    g.out = out; g.out_bf16 = out_bf16 ? 1 : 0;
+    g.out = out;
     g.out_codes = out_codes; g.out_scales = out_scales;
-    return launch_gemm(g, kEpiSwiglu, stream);
+    return launch_gemm(g, kEpiSwiglu, out_bf16, stream);
 }
 
 }  // namespace fp4dit

@@ -51,7 +51,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
     }
     amax = max_quad_u(amax);
     const uint32_t sc = e8m0_from_amax_bits(amax);
-    const uint32_t w = sc == 0xFFu ? 0u : e2m1_pack8(xb, sc);
+    float xf[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xf[i] = __uint_as_float(xb[i]);
+    const uint32_t w = sc == 0xFFu ? 0u : e2m1_pack8(xf, sc);
     reinterpret_cast<uint32_t*>(codes)[blk * 4 + part] = w;
     if (part == 0) scales[blk] = (uint8_t)sc;
 }
@@ -87,9 +90,12 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const void* __restrict
         amax = a > amax ? a : amax;
     }
     const uint32_t sc = e8m0_from_amax_bits(amax);
+    float xf[32];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) xf[r] = __uint_as_float(xb[r]);
     v4u out;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = sc == 0xFFu ? 0u : e2m1_pack8(xb + 8 * i, sc);
+    for (int i = 0; i < 4; ++i) out[i] = sc == 0xFFu ? 0u : e2m1_pack8(xf + 8 * i, sc);
     *reinterpret_cast<v4u*>(codes + p * (K / 2) + kb * 16) = out;
     scales[p * (K / 32) + kb] = (uint8_t)sc;
 }

@@ -27,24 +27,17 @@ typedef short v8s __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ void store_mx_block(const float* hv, int lane, bool live,
                                                uint8_t* codes16, uint8_t* scale1) {
     const int h = lane >> 5;
-    uint32_t hb[16];
     uint32_t amax = 0u;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        hb[i] = __float_as_uint(hv[i]);
-        const uint32_t a = hb[i] & 0x7FFFFFFFu;
+        const uint32_t a = __float_as_uint(hv[i]) & 0x7FFFFFFFu;
         amax = a > amax ? a : amax;
     }
     amax = max_xor32_u(amax);
     const uint32_t sc = e8m0_from_amax_bits(amax);
     uint32_t c16[4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        uint32_t w = 0u;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) w |= e2m1_code(hb[4 * a + r], sc) << (4 * r);
-        c16[a] = sc == 0xFFu ? 0u : w;
-    }
+    for (int a = 0; a < 4; ++a) c16[a] = sc == 0xFFu ? 0u : e2m1_pack4(hv + 4 * a, sc);
     const uint32_t send = h == 0 ? (c16[2] | (c16[3] << 16)) : (c16[0] | (c16[1] << 16));
     const uint32_t recv = partner_xor32(send, lane);
     v2u st;
