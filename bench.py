@@ -68,16 +68,14 @@ class Layer:
         wd = torch.from_numpy(w).to(dev, torch.float32)
         if self.t is not None:
             wd = ops.fold_inverse_transform(wd, self.t)
-        self.b_codes, self.b_scales = ops.pack_weight(wd, interleave_group=group)
+        self.b = ops.pack_weight(wd, interleave_group=group)          # tiled MXFP4 [N, K]
         del wd
-        self.n = self.b_codes.shape[0]
-        self.a_codes = torch.empty((self.m, self.k // 2), dtype=torch.uint8, device=dev)
-        self.a_scales = torch.empty((self.m, self.k // 32), dtype=torch.uint8, device=dev)
+        self.n = self.b.rows
+        self.a = ops.mx_empty(self.m, self.k, "tiled", dev)
         if wl.epilogue == "swiglu":
             self.out = torch.empty((self.m, self.n // 2), dtype=torch.bfloat16, device=dev) \
                 if not wl.requant else None
-            self.codes = torch.empty((self.m, self.n // 4), dtype=torch.uint8, device=dev) if wl.requant else None
-            self.scales = torch.empty((self.m, self.n // 64), dtype=torch.uint8, device=dev) if wl.requant else None
+            self.req = ops.mx_empty(self.m, self.n // 2, "tiled", dev) if wl.requant else None
         else:
             self.out = torch.empty((self.m, self.n), dtype=torch.bfloat16, device=dev)
         if wl.epilogue == "rmsnorm_head":
@@ -88,21 +86,20 @@ class Layer:
     def quantize(self, step):
         x = self.xs[step % len(self.xs)]
         if self.t is not None:
-            self.ops.block_transform(x, self.t, quantize=True, out=(None, self.a_codes, self.a_scales))
+            self.ops.block_transform(x, self.t, quantize=True, out=self.a)
         else:
-            self.ops.quantize_mxfp4(x, self.a_codes, self.a_scales)
+            self.ops.quantize_mxfp4(x, out=self.a)
 
     def gemm(self):
         ops, wl = self.ops, self.wl
         if wl.epilogue == "rmsnorm_head":
-            ops.gemm_fp4_epilogue_rmsnorm_head(self.a_codes, self.a_scales, self.b_codes, self.b_scales,
-                                               wl.head_dim, wl.n_norm, self.norm_w, wl.eps, out=self.out)
+            ops.gemm_fp4_epilogue_rmsnorm_head(self.a, self.b, wl.head_dim, wl.n_norm, self.norm_w, wl.eps,
+                                               out=self.out)
         elif wl.epilogue == "swiglu":
-            ops.gemm_fp4_epilogue_swiglu(self.a_codes, self.a_scales, self.b_codes, self.b_scales,
-                                         out_dtype=torch_bf16(), requant=wl.requant,
-                                         out=(self.out, self.codes, self.scales))
+            ops.gemm_fp4_epilogue_swiglu(self.a, self.b, out_dtype=None, requant=wl.requant, out=self.out,
+                                         out_mx=self.req)
         else:
-            ops.gemm_fp4_epilogue_none(self.a_codes, self.a_scales, self.b_codes, self.b_scales, out=self.out)
+            ops.gemm_fp4_epilogue_none(self.a, self.b, out=self.out)
 
     def quant_bytes(self):
         """Algorithmic HBM bytes of the activation quantiser: bf16 in, codes + scales out."""
@@ -119,11 +116,6 @@ class Layer:
         return ab + bb + ob
 
 
-def torch_bf16():
-    import torch
-    return torch.bfloat16
-
-
 def build_layers(args, ops, torch, workloads):
     if args.workload == "dit_1k_linears":
         wls = [workloads.qkv_hd128(), workloads.qkv_hd256(), workloads.ffn_up_swiglu(requant=True)]
@@ -136,7 +128,7 @@ def build_layers(args, ops, torch, workloads):
     up_layer.wl.requant = False
     n_half = up_layer.n // 2
     up_layer.out = torch.empty((up_layer.m, n_half), dtype=torch.bfloat16, device="cuda")
-    up_layer.codes = up_layer.scales = None
+    up_layer.req = None
     down.x = np.zeros((down.m, down.k), dtype=np.float32)          # placeholder: replaced below
     dl = Layer("dit_block_down", down, ops, torch, 1, transform=down.t)
     dl.xs = [up_layer.out]

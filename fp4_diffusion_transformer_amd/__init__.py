@@ -8,6 +8,8 @@ and its absence raises: there is no CPU fallback.
 
 from .ops import (  # noqa: F401
     Fp4ditError,
+    MxTensor,
+    mx_empty,
     block_transform,
     fold_inverse_transform,
     gemm_fp4_epilogue_none,

@@ -15,16 +15,18 @@ using fp4dit::kGemmNMultiple;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 bool valid_dtype(fp4dit_dtype d) { return d == FP4DIT_F32 || d == FP4DIT_BF16; }
+bool valid_layout(fp4dit_layout l) { return l == FP4DIT_MX_ROWMAJOR || l == FP4DIT_MX_TILED; }
 fp4dit_status launched(hipError_t e) { return e == hipSuccess ? FP4DIT_OK : FP4DIT_E_LAUNCH; }
 
-// Byte offsets inside the GEMM operands are 32-bit.
+// Byte offsets inside the GEMM operands are 32-bit (tiled buffers are padded
+// to an even number of rows).
 constexpr int64_t kMaxOperandBytes = (int64_t(1) << 31) - 1;
 
 fp4dit_status check_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
                          const uint8_t* bc, const uint8_t* bs) {
     if (M < 0 || N <= 0 || K <= 0) return FP4DIT_E_SHAPE;
     if (N % kGemmNMultiple != 0 || K % kGemmKMultiple != 0) return FP4DIT_E_SHAPE;
-    if (M * (K / 2) > kMaxOperandBytes || N * (K / 2) > kMaxOperandBytes) return FP4DIT_E_SHAPE;
+    if ((M + 1) * (K / 2) > kMaxOperandBytes || N * (K / 2) > kMaxOperandBytes) return FP4DIT_E_SHAPE;
     if (M == 0) return FP4DIT_OK;
     if (!ac || !as || !bc || !bs) return FP4DIT_E_NULL;
     if (!aligned(ac, 16) || !aligned(bc, 16) || !aligned(as, 4) || !aligned(bs, 4)) return FP4DIT_E_ALIGN;
@@ -50,22 +52,25 @@ const char* fp4dit_status_string(fp4dit_status s) {
 int32_t fp4dit_swiglu_interleave_group(void) { return fp4dit::kSwigluGroup; }
 
 fp4dit_status fp4dit_quantize_mxfp4(const void* x, fp4dit_dtype x_dtype, int64_t rows, int64_t cols,
-                                    uint8_t* codes, uint8_t* scales, hipStream_t stream) {
-    if (!valid_dtype(x_dtype)) return FP4DIT_E_UNSUPPORTED;
-    if (rows < 0 || cols < 0 || cols % 32 != 0) return FP4DIT_E_SHAPE;
+                                    uint8_t* codes, uint8_t* scales, fp4dit_layout layout, hipStream_t stream) {
+    if (!valid_dtype(x_dtype) || !valid_layout(layout)) return FP4DIT_E_UNSUPPORTED;
+    if (rows < 0 || cols < 0 || cols % (layout == FP4DIT_MX_TILED ? 128 : 32) != 0) return FP4DIT_E_SHAPE;
     if (rows == 0 || cols == 0) return FP4DIT_OK;
-    if (rows * (cols / 32) > (int64_t(1) << 36)) return FP4DIT_E_SHAPE;
+    if (rows * (cols / 32) >= (int64_t(1) << 32)) return FP4DIT_E_SHAPE;
     if (!x || !codes || !scales) return FP4DIT_E_NULL;
     if (!aligned(x, 16) || !aligned(codes, 16)) return FP4DIT_E_ALIGN;
-    return launched(fp4dit::launch_quantize(x, x_dtype == FP4DIT_BF16, rows, cols, codes, scales, stream));
+    return launched(fp4dit::launch_quantize(x, x_dtype == FP4DIT_BF16, rows, cols, codes, scales,
+                                            layout == FP4DIT_MX_TILED, stream));
 }
 
 fp4dit_status fp4dit_block_transform(const void* x, fp4dit_dtype x_dtype, int64_t rows, int64_t cols,
                                      const uint16_t* t_bf16, int64_t n_t, void* y, fp4dit_dtype y_dtype,
-                                     uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+                                     uint8_t* codes, uint8_t* scales, fp4dit_layout layout, hipStream_t stream) {
     if (!valid_dtype(x_dtype) || (y && !valid_dtype(y_dtype))) return FP4DIT_E_UNSUPPORTED;
     if ((codes == nullptr) != (scales == nullptr)) return FP4DIT_E_UNSUPPORTED;
+    if (codes && !valid_layout(layout)) return FP4DIT_E_UNSUPPORTED;
     if (rows < 0 || cols < 0 || cols % 32 != 0) return FP4DIT_E_SHAPE;
+    if (codes && layout == FP4DIT_MX_TILED && cols % 128 != 0) return FP4DIT_E_SHAPE;
     if (n_t != 1 && n_t != cols / 32) return FP4DIT_E_SHAPE;
     if (rows == 0 || cols == 0) return FP4DIT_OK;
     if (cols / 32 > (int64_t(1) << 20) || rows > (int64_t(1) << 23)) return FP4DIT_E_SHAPE;  // grid.y <= 65535
@@ -74,7 +79,8 @@ fp4dit_status fp4dit_block_transform(const void* x, fp4dit_dtype x_dtype, int64_
     if (!aligned(x, 16) || !aligned(t_bf16, 2) || (y && !aligned(y, 16)) || (codes && !aligned(codes, 16)))
         return FP4DIT_E_ALIGN;
     return launched(fp4dit::launch_block_transform(x, x_dtype == FP4DIT_BF16, rows, cols, t_bf16, n_t, y,
-                                                   y_dtype == FP4DIT_BF16, codes, scales, stream));
+                                                   y_dtype == FP4DIT_BF16, codes, scales,
+                                                   layout == FP4DIT_MX_TILED, stream));
 }
 
 fp4dit_status fp4dit_fold_inverse_transform(const float* w, int64_t K, int64_t N, const uint16_t* t_bf16,
@@ -91,17 +97,17 @@ fp4dit_status fp4dit_fold_inverse_transform(const float* w, int64_t K, int64_t N
 
 fp4dit_status fp4dit_pack_weight(const void* w, fp4dit_dtype w_dtype, int64_t K, int64_t N,
                                  int32_t interleave_group, uint8_t* codes, uint8_t* scales,
-                                 hipStream_t stream) {
-    if (!valid_dtype(w_dtype)) return FP4DIT_E_UNSUPPORTED;
+                                 fp4dit_layout layout, hipStream_t stream) {
+    if (!valid_dtype(w_dtype) || !valid_layout(layout)) return FP4DIT_E_UNSUPPORTED;
     if (interleave_group < 0) return FP4DIT_E_UNSUPPORTED;
-    if (K < 0 || N < 0 || K % 32 != 0) return FP4DIT_E_SHAPE;
+    if (K < 0 || N < 0 || K % (layout == FP4DIT_MX_TILED ? 128 : 32) != 0) return FP4DIT_E_SHAPE;
     if (interleave_group > 0 && N % (2 * (int64_t)interleave_group) != 0) return FP4DIT_E_SHAPE;
     if (K == 0 || N == 0) return FP4DIT_OK;
     if (K / 32 > 65535) return FP4DIT_E_SHAPE;
     if (!w || !codes || !scales) return FP4DIT_E_NULL;
     if (!aligned(codes, 16) || !aligned(w, w_dtype == FP4DIT_BF16 ? 2 : 4)) return FP4DIT_E_ALIGN;
     return launched(fp4dit::launch_pack_weight(w, w_dtype == FP4DIT_BF16, K, N, interleave_group, codes,
-                                               scales, stream));
+                                               scales, layout == FP4DIT_MX_TILED, stream));
 }
 
 fp4dit_status fp4dit_gemm_fp4_epilogue_none(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,

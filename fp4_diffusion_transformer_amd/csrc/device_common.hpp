@@ -72,6 +72,19 @@ __device__ __forceinline__ uint32_t e2m1_pack4(const float* x, uint32_t scale_by
     return w & 0xFFFFu;
 }
 
+// ------------------------------------------------------- tiled layout ----
+// Byte offsets in the MX_TILED layout of a [rows][cols] MXFP4 matrix
+// (cols % 128 == 0): codes in 128-byte tiles of 2 rows x 128 elements,
+// scales in 128-byte tiles of 32 rows x 4 blocks (see include/fp4dit.h).
+// tiled_code_off: byte holding elements (k, k+1) of row r, k even.
+__device__ __forceinline__ int64_t tiled_code_off(int64_t r, int64_t k, int64_t cols) {
+    return (((r >> 1) * (cols >> 7) + (k >> 7)) << 7) + ((r & 1) << 6) + ((k & 127) >> 1);
+}
+// tiled_scale_off: scale byte of row r, 32-element block b.
+__device__ __forceinline__ int64_t tiled_scale_off(int64_t r, int64_t b, int64_t cols) {
+    return (((r >> 5) * (cols >> 7) + (b >> 2)) << 7) + ((r & 31) << 2) + (b & 3);
+}
+
 // ---------------------------------------------------------------- bf16 ----
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     uint32_t u = __float_as_uint(f);

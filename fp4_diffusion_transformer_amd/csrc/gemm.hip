@@ -111,36 +111,45 @@ struct LoadPlan {
     uint32_t w_scale, x_scale;
 };
 
+// Operands are MX_TILED: K stage kt of rows (2p, 2p+1) is one 128-byte code
+// tile at ((p * K/128) + kt) * 128, and stage kt of 32 rows is one 128-byte
+// scale tile, so every load fetches whole cache lines.
+__device__ __forceinline__ uint32_t code_tile_off(uint32_t r, uint32_t kq) {
+    return ((r >> 1) * kq) * 128 + (r & 1) * 64;
+}
+__device__ __forceinline__ uint32_t scale_tile_off(uint32_t r, uint32_t kq) {
+    return ((r >> 5) * kq) * 128 + (r & 31) * 4;
+}
+
 __device__ __forceinline__ LoadPlan make_plan(const GemmArgs& g, int64_t n0, int64_t m0, int wave, int lane) {
     LoadPlan p;
-    const uint32_t kcb = (uint32_t)(g.K / 2);
-    const uint32_t ksb = (uint32_t)(g.K / 32);
+    const uint32_t kq = (uint32_t)(g.K / 128);          // K stages (tiles per row pair / row block)
     const int rin = lane >> 2;                          // row within a 16-row group
     const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);  // chunk for physical slot lane & 3
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int row = (wave * 4 + j) * 16 + rin;
-        p.w_code[j] = (uint32_t)(n0 + row) * kcb + lchunk * 16;
+        p.w_code[j] = code_tile_off((uint32_t)(n0 + row), kq) + lchunk * 16;
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int row = (wave * 2 + j) * 16 + rin;
         int64_t xr = m0 + row;
         xr = xr < g.M ? xr : g.M - 1;                   // ragged token tile: clamp, never stored
-        p.x_code[j] = (uint32_t)xr * kcb + lchunk * 16;
+        p.x_code[j] = code_tile_off((uint32_t)xr, kq) + lchunk * 16;
     }
-    p.w_scale = (uint32_t)(n0 + wave * 64 + lane) * ksb;
+    p.w_scale = scale_tile_off((uint32_t)(n0 + wave * 64 + lane), kq);
     int64_t xr = m0 + wave * 32 + (lane & 31);          // lanes 32..63 repeat lanes 0..31
     xr = xr < g.M ? xr : g.M - 1;
-    p.x_scale = (uint32_t)xr * ksb;
+    p.x_scale = scale_tile_off((uint32_t)xr, kq);
     return p;
 }
 
 // Enqueue the 8 direct-to-LDS loads of K stage kt into `stage` (this wave's share).
 __device__ __forceinline__ void issue_stage(uint8_t* stage, const GemmArgs& g, const LoadPlan& p, int kt,
                                             int wave, int lane) {
-    const uint8_t* wc = g.b_codes + (int64_t)kt * kRowBytes;
-    const uint8_t* xc = g.a_codes + (int64_t)kt * kRowBytes;
+    const uint8_t* wc = g.b_codes + (int64_t)kt * 128;
+    const uint8_t* xc = g.a_codes + (int64_t)kt * 128;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
         __builtin_amdgcn_global_load_lds(wc + p.w_code[j], (lds_void*)(stage + kWCodesOff + (wave * 4 + j) * 1024),
@@ -149,10 +158,10 @@ __device__ __forceinline__ void issue_stage(uint8_t* stage, const GemmArgs& g, c
     for (int j = 0; j < 2; ++j)
         __builtin_amdgcn_global_load_lds(xc + p.x_code[j], (lds_void*)(stage + kXCodesOff + (wave * 2 + j) * 1024),
                                          16, 0, 0);
-    __builtin_amdgcn_global_load_lds(g.b_scales + (int64_t)kt * kScaleBytes + p.w_scale,
+    __builtin_amdgcn_global_load_lds(g.b_scales + (int64_t)kt * 128 + p.w_scale,
                                      (lds_void*)(stage + kWScalesOff + wave * 256), 4, 0, 0);
     // 128 token rows of scales: 32 per wave, into the wave's 256-byte slot
-    __builtin_amdgcn_global_load_lds(g.a_scales + (int64_t)kt * kScaleBytes + p.x_scale,
+    __builtin_amdgcn_global_load_lds(g.a_scales + (int64_t)kt * 128 + p.x_scale,
                                      (lds_void*)(stage + kXScalesOff + wave * 256), 4, 0, 0);
 }
 
@@ -511,10 +520,10 @@ __global__ __launch_bounds__(256, 2) void gemm_fp4_kernel(GemmArgs g) {
                         st[0] = (recv & 0xFFFFu) | (c16[2] << 16);
                         st[1] = (recv >> 16) | (c16[3] << 16);
                     }
-                    if (tok < g.M) {
+                    if (tok < g.M) {                  // MX_TILED output, ready for the next GEMM
                         const int64_t blk = ob0 / 32 + p;
-                        *reinterpret_cast<v2u*>(g.out_codes + tok * (nh / 2) + blk * 16 + h * 8) = st;
-                        if (h == 0) g.out_scales[tok * (nh / 32) + blk] = (uint8_t)sc;
+                        *reinterpret_cast<v2u*>(g.out_codes + tiled_code_off(tok, blk * 32, nh) + h * 8) = st;
+                        if (h == 0) g.out_scales[tiled_scale_off(tok, blk, nh)] = (uint8_t)sc;
                     }
                 }
             }

@@ -9,14 +9,14 @@
 namespace fp4dit {
 
 hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols,
-                           uint8_t* codes, uint8_t* scales, hipStream_t stream);
+                           uint8_t* codes, uint8_t* scales, bool tiled, hipStream_t stream);
 
 hipError_t launch_pack_weight(const void* w, bool bf16, int64_t K, int64_t N, int group,
-                              uint8_t* codes, uint8_t* scales, hipStream_t stream);
+                              uint8_t* codes, uint8_t* scales, bool tiled, hipStream_t stream);
 
 hipError_t launch_block_transform(const void* x, bool x_bf16, int64_t rows, int64_t cols,
                                   const uint16_t* t, int64_t n_t, void* y, bool y_bf16,
-                                  uint8_t* codes, uint8_t* scales, hipStream_t stream);
+                                  uint8_t* codes, uint8_t* scales, bool tiled, hipStream_t stream);
 
 hipError_t launch_fold_inverse(const float* w, int64_t K, int64_t N, const uint16_t* t, int64_t n_t,
                                float* w_out, hipStream_t stream);

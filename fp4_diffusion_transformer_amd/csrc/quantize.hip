@@ -16,11 +16,11 @@
 
 namespace fp4dit {
 
-template <bool kBf16>
+template <bool kBf16, bool kTiled>
 __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ x,
                                                        uint8_t* __restrict__ codes,
                                                        uint8_t* __restrict__ scales,
-                                                       int64_t nblocks) {
+                                                       int64_t nblocks, int64_t cols) {
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t blk = gid >> 2;
     const int part = (int)(gid & 3);
@@ -55,13 +55,20 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 8; ++i) xf[i] = __uint_as_float(xb[i]);
     const uint32_t w = sc == 0xFFu ? 0u : e2m1_pack8(xf, sc);
-    reinterpret_cast<uint32_t*>(codes)[blk * 4 + part] = w;
-    if (part == 0) scales[blk] = (uint8_t)sc;
+    if (kTiled) {
+        const uint32_t nbr = (uint32_t)(cols >> 5);              // blocks per row (nblocks < 2^32)
+        const uint32_t row = (uint32_t)blk / nbr, b = (uint32_t)blk - row * nbr;
+        *reinterpret_cast<uint32_t*>(codes + tiled_code_off(row, (int64_t)b * 32 + part * 8, cols)) = w;
+        if (part == 0) scales[tiled_scale_off(row, b, cols)] = (uint8_t)sc;
+    } else {
+        reinterpret_cast<uint32_t*>(codes)[blk * 4 + part] = w;
+        if (part == 0) scales[blk] = (uint8_t)sc;
+    }
 }
 
 // One thread per output block (physical column p, K-block kb): gathers the 32
 // weights of logical column src(p), rows 32kb..32kb+31, and encodes them.
-template <bool kBf16>
+template <bool kBf16, bool kTiled>
 __global__ __launch_bounds__(256) void pack_weight_kernel(const void* __restrict__ w,
                                                           int64_t K, int64_t N, int group,
                                                           uint8_t* __restrict__ codes,
@@ -96,31 +103,42 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const void* __restrict
     v4u out;
 #pragma unroll
     for (int i = 0; i < 4; ++i) out[i] = sc == 0xFFu ? 0u : e2m1_pack8(xf + 8 * i, sc);
-    *reinterpret_cast<v4u*>(codes + p * (K / 2) + kb * 16) = out;
-    scales[p * (K / 32) + kb] = (uint8_t)sc;
+    if (kTiled) {
+        *reinterpret_cast<v4u*>(codes + tiled_code_off(p, kb * 32, K)) = out;
+        scales[tiled_scale_off(p, kb, K)] = (uint8_t)sc;
+    } else {
+        *reinterpret_cast<v4u*>(codes + p * (K / 2) + kb * 16) = out;
+        scales[p * (K / 32) + kb] = (uint8_t)sc;
+    }
 }
 
 hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols,
-                           uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+                           uint8_t* codes, uint8_t* scales, bool tiled, hipStream_t stream) {
     const int64_t nblocks = rows * (cols / 32);
     const int64_t threads = nblocks * 4;
     const dim3 grid((unsigned)((threads + 255) / 256));
+#define FP4DIT_Q(B, T) \
+    hipLaunchKernelGGL((quantize_kernel<B, T>), grid, dim3(256), 0, stream, x, codes, scales, nblocks, cols)
     if (bf16) {
-        hipLaunchKernelGGL(quantize_kernel<true>, grid, dim3(256), 0, stream, x, codes, scales, nblocks);
+        if (tiled) FP4DIT_Q(true, true); else FP4DIT_Q(true, false);
     } else {
-        hipLaunchKernelGGL(quantize_kernel<false>, grid, dim3(256), 0, stream, x, codes, scales, nblocks);
+        if (tiled) FP4DIT_Q(false, true); else FP4DIT_Q(false, false);
     }
+#undef FP4DIT_Q
     return hipGetLastError();
 }
 
 hipError_t launch_pack_weight(const void* w, bool bf16, int64_t K, int64_t N, int group,
-                              uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+                              uint8_t* codes, uint8_t* scales, bool tiled, hipStream_t stream) {
     const dim3 grid((unsigned)((N + 255) / 256), (unsigned)(K / 32));
+#define FP4DIT_P(B, T) \
+    hipLaunchKernelGGL((pack_weight_kernel<B, T>), grid, dim3(256), 0, stream, w, K, N, group, codes, scales)
     if (bf16) {
-        hipLaunchKernelGGL(pack_weight_kernel<true>, grid, dim3(256), 0, stream, w, K, N, group, codes, scales);
+        if (tiled) FP4DIT_P(true, true); else FP4DIT_P(true, false);
     } else {
-        hipLaunchKernelGGL(pack_weight_kernel<false>, grid, dim3(256), 0, stream, w, K, N, group, codes, scales);
+        if (tiled) FP4DIT_P(false, true); else FP4DIT_P(false, false);
     }
+#undef FP4DIT_P
     return hipGetLastError();
 }
 

@@ -56,7 +56,7 @@ __device__ __forceinline__ void store_mx_block(const float* hv, int lane, bool l
 
 constexpr int kTokIters = 4;           // 32-token groups per wave
 
-template <bool kXBf16, bool kYBf16>
+template <bool kXBf16, bool kYBf16, bool kTiled>
 __global__ __launch_bounds__(256) void block_transform_kernel(const void* __restrict__ x, int64_t rows,
                                                               int64_t cols, const uint16_t* __restrict__ t,
                                                               int64_t n_t, void* __restrict__ y,
@@ -136,7 +136,11 @@ __global__ __launch_bounds__(256) void block_transform_kernel(const void* __rest
                 }
             }
             if (codes != nullptr) {
-                store_mx_block(hv, lane, live, codes + tok * (cols / 2) + b * 16, scales + tok * nblk + b);
+                if (kTiled)
+                    store_mx_block(hv, lane, live, codes + tiled_code_off(tok, b * 32, cols),
+                                   scales + tiled_scale_off(tok, b, cols));
+                else
+                    store_mx_block(hv, lane, live, codes + tok * (cols / 2) + b * 16, scales + tok * nblk + b);
             }
         }
     }
@@ -204,18 +208,22 @@ __global__ __launch_bounds__(256) void fold_inverse_kernel(const float* __restri
 
 hipError_t launch_block_transform(const void* x, bool x_bf16, int64_t rows, int64_t cols,
                                   const uint16_t* t, int64_t n_t, void* y, bool y_bf16,
-                                  uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+                                  uint8_t* codes, uint8_t* scales, bool tiled, hipStream_t stream) {
     const int64_t nblk = cols / 32;
     const int64_t wg_cols = (nblk + 15) / 16;                  // 4 waves x 4 blocks per workgroup
     const int64_t wg_rows = (rows + 32 * kTokIters - 1) / (32 * kTokIters);
     const dim3 grid((unsigned)wg_cols, (unsigned)wg_rows);
-#define FP4DIT_LAUNCH_BT(XB, YB) \
-    hipLaunchKernelGGL((block_transform_kernel<XB, YB>), grid, dim3(256), 0, stream, x, rows, cols, t, n_t, y, codes, scales)
+#define FP4DIT_LAUNCH_BT(XB, YB, T) \
+    hipLaunchKernelGGL((block_transform_kernel<XB, YB, T>), grid, dim3(256), 0, stream, x, rows, cols, t, n_t, y, \
+                       codes, scales)
+#define FP4DIT_LAUNCH_BT2(XB, YB) \
+    if (tiled) FP4DIT_LAUNCH_BT(XB, YB, true); else FP4DIT_LAUNCH_BT(XB, YB, false)
     if (x_bf16) {
-        if (y_bf16) FP4DIT_LAUNCH_BT(true, true); else FP4DIT_LAUNCH_BT(true, false);
+        if (y_bf16) { FP4DIT_LAUNCH_BT2(true, true); } else { FP4DIT_LAUNCH_BT2(true, false); }
     } else {
-        if (y_bf16) FP4DIT_LAUNCH_BT(false, true); else FP4DIT_LAUNCH_BT(false, false);
+        if (y_bf16) { FP4DIT_LAUNCH_BT2(false, true); } else { FP4DIT_LAUNCH_BT2(false, false); }
     }
+#undef FP4DIT_LAUNCH_BT2
 #undef FP4DIT_LAUNCH_BT
     return hipGetLastError();
 }

@@ -8,6 +8,7 @@ the library is missing or a call fails, an exception is raised.
 
 import ctypes
 import os
+from typing import NamedTuple, Optional
 
 import torch
 
@@ -15,6 +16,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 
 F32 = 0
 BF16 = 1
+ROWMAJOR = 0
+TILED = 1
+_LAYOUTS = {"rowmajor": ROWMAJOR, "tiled": TILED}
 _STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape", 3: "misaligned pointer",
            4: "unsupported argument", 5: "kernel launch failed"}
 
@@ -42,10 +46,10 @@ def lib():
         L = ctypes.CDLL(path)
         P, I64, I32, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
         sig = {
-            "fp4dit_quantize_mxfp4": [P, I32, I64, I64, P, P, P],
-            "fp4dit_block_transform": [P, I32, I64, I64, P, I64, P, I32, P, P, P],
+            "fp4dit_quantize_mxfp4": [P, I32, I64, I64, P, P, I32, P],
+            "fp4dit_block_transform": [P, I32, I64, I64, P, I64, P, I32, P, P, I32, P],
             "fp4dit_fold_inverse_transform": [P, I64, I64, P, I64, P, P],
-            "fp4dit_pack_weight": [P, I32, I64, I64, I32, P, P, P],
+            "fp4dit_pack_weight": [P, I32, I64, I64, I32, P, P, I32, P],
             "fp4dit_gemm_fp4_epilogue_none": [I64, I64, I64, P, P, P, P, P, I32, P],
             "fp4dit_gemm_fp4_epilogue_rmsnorm_head": [I64, I64, I64, P, P, P, P, I32, I64, P, F, P, I32, P],
             "fp4dit_gemm_fp4_epilogue_swiglu": [I64, I64, I64, P, P, P, P, P, I32, P, P, P],
@@ -96,42 +100,68 @@ def swiglu_interleave_group():
     return int(lib().fp4dit_swiglu_interleave_group())
 
 
-def quantize_mxfp4(x, codes=None, scales=None):
-    """x [rows, cols] float32/bfloat16 -> (codes uint8 [rows, cols/2], scales uint8 [rows, cols/32])."""
+class MxTensor(NamedTuple):
+    """An MXFP4 matrix [rows, cols]: codes and e8m0 scales in `layout`.
+
+    For "tiled" the buffers are padded (codes to an even number of rows,
+    scales to a multiple of 32 rows), so rows/cols are the logical shape.
+    """
+    codes: torch.Tensor
+    scales: torch.Tensor
+    rows: int
+    cols: int
+    layout: str = "tiled"
+
+
+def _round_up(v, m):
+    return (v + m - 1) // m * m
+
+
+def mx_empty(rows, cols, layout="tiled", device="cuda"):
+    """Allocate an MxTensor of the right storage size for `layout`."""
+    if layout == "tiled":
+        codes = torch.empty((_round_up(rows, 2), cols // 2), dtype=torch.uint8, device=device)
+        scales = torch.empty((_round_up(rows, 32), cols // 32), dtype=torch.uint8, device=device)
+    elif layout == "rowmajor":
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=device)
+        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=device)
+    else:
+        raise ValueError("layout must be 'tiled' or 'rowmajor'")
+    return MxTensor(codes, scales, rows, cols, layout)
+
+
+def quantize_mxfp4(x, layout="tiled", out: Optional[MxTensor] = None):
+    """x [rows, cols] float32/bfloat16 -> MxTensor."""
     _dev(x, "x")
     rows, cols = x.shape
-    if codes is None:
-        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
-    if scales is None:
-        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
-    _call("fp4dit_quantize_mxfp4", _ptr(x), _dtype_code(x.dtype), rows, cols, _ptr(codes), _ptr(scales),
-          _stream())
-    return codes, scales
+    mx = out if out is not None else mx_empty(rows, cols, layout, x.device)
+    _call("fp4dit_quantize_mxfp4", _ptr(x), _dtype_code(x.dtype), rows, cols, _ptr(mx.codes), _ptr(mx.scales),
+          _LAYOUTS[mx.layout], _stream())
+    return mx
 
 
-def block_transform(x, t, y_dtype=None, quantize=True, out=None):
+def block_transform(x, t, y_dtype=None, quantize=True, layout="tiled", y=None, out: Optional[MxTensor] = None):
     """y_b = x_b @ T_b per 32-element block.  t: bfloat16 [n_t, 32, 32].
 
-    Returns (y or None, codes or None, scales or None); y is produced when
-    y_dtype (float32 / bfloat16) is given, codes/scales when quantize is set.
-    `out` optionally supplies preallocated (y, codes, scales).
+    Returns (y or None, MxTensor or None): y is produced when y_dtype
+    (float32 / bfloat16) or a y tensor is given, the MXFP4 encoding of the
+    product when quantize is set (into `out` if given).
     """
     _dev(x, "x")
     _dev(t, "t")
     if t.dtype != torch.bfloat16:
         raise ValueError("t must be bfloat16")
     rows, cols = x.shape
-    y = codes = scales = None
-    if out is not None:
-        y, codes, scales = out
-    if y_dtype is not None and y is None:
+    if y is None and y_dtype is not None:
         y = torch.empty((rows, cols), dtype=y_dtype, device=x.device)
-    if quantize and codes is None:
-        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
-        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    mx = None
+    if quantize:
+        mx = out if out is not None else mx_empty(rows, cols, layout, x.device)
     _call("fp4dit_block_transform", _ptr(x), _dtype_code(x.dtype), rows, cols, _ptr(t), t.shape[0],
-          _ptr(y), _dtype_code(y.dtype) if y is not None else F32, _ptr(codes), _ptr(scales), _stream())
-    return y, codes, scales
+          _ptr(y), _dtype_code(y.dtype) if y is not None else F32,
+          _ptr(mx.codes) if mx else None, _ptr(mx.scales) if mx else None,
+          _LAYOUTS[mx.layout] if mx else TILED, _stream())
+    return y, mx
 
 
 def fold_inverse_transform(w, t):
@@ -146,70 +176,69 @@ def fold_inverse_transform(w, t):
     return out
 
 
-def pack_weight(w, interleave_group=0):
-    """Logical weight w [K, N] -> MXFP4 codes [N, K/2] and scales [N, K/32].
+def pack_weight(w, interleave_group=0, layout="tiled"):
+    """Logical weight w [K, N] -> MXFP4 [N, K] (rows = physical output columns).
 
     interleave_group > 0 treats w as [gate | up] and interleaves the columns
     for the SwiGLU epilogue (use swiglu_interleave_group()).
     """
     _dev(w, "w")
     k, n = w.shape
-    codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
-    scales = torch.empty((n, k // 32), dtype=torch.uint8, device=w.device)
-    _call("fp4dit_pack_weight", _ptr(w), _dtype_code(w.dtype), k, n, int(interleave_group), _ptr(codes),
-          _ptr(scales), _stream())
-    return codes, scales
+    mx = mx_empty(n, k, layout, w.device)
+    _call("fp4dit_pack_weight", _ptr(w), _dtype_code(w.dtype), k, n, int(interleave_group), _ptr(mx.codes),
+          _ptr(mx.scales), _LAYOUTS[layout], _stream())
+    return mx
 
 
-def _gemm_shapes(a_codes, a_scales, b_codes, b_scales):
-    for t, nm in ((a_codes, "a_codes"), (a_scales, "a_scales"), (b_codes, "b_codes"), (b_scales, "b_scales")):
+def _gemm_shapes(a: MxTensor, b: MxTensor):
+    for t, nm in ((a.codes, "a.codes"), (a.scales, "a.scales"), (b.codes, "b.codes"), (b.scales, "b.scales")):
         _dev(t, nm)
         if t.dtype != torch.uint8:
             raise ValueError(nm + " must be uint8")
-    m, k2 = a_codes.shape
-    n = b_codes.shape[0]
-    if b_codes.shape[1] != k2:
+    if a.layout != "tiled" or b.layout != "tiled":
+        raise ValueError("GEMM operands must be in the tiled layout")
+    if a.cols != b.cols:
         raise ValueError("A and B disagree on K")
-    return m, n, 2 * k2
+    return a.rows, b.rows, a.cols
 
 
-def gemm_fp4_epilogue_none(a_codes, a_scales, b_codes, b_scales, out_dtype=torch.bfloat16, out=None):
-    m, n, k = _gemm_shapes(a_codes, a_scales, b_codes, b_scales)
+def gemm_fp4_epilogue_none(a: MxTensor, b: MxTensor, out_dtype=torch.bfloat16, out=None):
+    m, n, k = _gemm_shapes(a, b)
     if out is None:
-        out = torch.empty((m, n), dtype=out_dtype, device=a_codes.device)
-    _call("fp4dit_gemm_fp4_epilogue_none", m, n, k, _ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales),
+        out = torch.empty((m, n), dtype=out_dtype, device=a.codes.device)
+    _call("fp4dit_gemm_fp4_epilogue_none", m, n, k, _ptr(a.codes), _ptr(a.scales), _ptr(b.codes), _ptr(b.scales),
           _ptr(out), _dtype_code(out.dtype), _stream())
     return out
 
 
-def gemm_fp4_epilogue_rmsnorm_head(a_codes, a_scales, b_codes, b_scales, head_dim, n_norm_cols, norm_w,
-                                   eps=1e-6, out_dtype=torch.bfloat16, out=None):
-    m, n, k = _gemm_shapes(a_codes, a_scales, b_codes, b_scales)
+def gemm_fp4_epilogue_rmsnorm_head(a: MxTensor, b: MxTensor, head_dim, n_norm_cols, norm_w, eps=1e-6,
+                                   out_dtype=torch.bfloat16, out=None):
+    m, n, k = _gemm_shapes(a, b)
     if norm_w is not None:
         _dev(norm_w, "norm_w")
         if norm_w.dtype != torch.float32:
             raise ValueError("norm_w must be float32")
     if out is None:
-        out = torch.empty((m, n), dtype=out_dtype, device=a_codes.device)
-    _call("fp4dit_gemm_fp4_epilogue_rmsnorm_head", m, n, k, _ptr(a_codes), _ptr(a_scales), _ptr(b_codes),
-          _ptr(b_scales), int(head_dim), int(n_norm_cols), _ptr(norm_w), float(eps), _ptr(out),
+        out = torch.empty((m, n), dtype=out_dtype, device=a.codes.device)
+    _call("fp4dit_gemm_fp4_epilogue_rmsnorm_head", m, n, k, _ptr(a.codes), _ptr(a.scales), _ptr(b.codes),
+          _ptr(b.scales), int(head_dim), int(n_norm_cols), _ptr(norm_w), float(eps), _ptr(out),
           _dtype_code(out.dtype), _stream())
     return out
 
 
-def gemm_fp4_epilogue_swiglu(a_codes, a_scales, b_codes, b_scales, out_dtype=torch.bfloat16, requant=False,
-                             out=None):
-    """SwiGLU over an interleaved weight: returns (h or None, codes or None, scales or None)."""
-    m, n, k = _gemm_shapes(a_codes, a_scales, b_codes, b_scales)
-    h = codes = scales = None
-    if out is not None:
-        h, codes, scales = out
-    if out_dtype is not None and h is None:
-        h = torch.empty((m, n // 2), dtype=out_dtype, device=a_codes.device)
-    if requant and codes is None:
-        codes = torch.empty((m, n // 4), dtype=torch.uint8, device=a_codes.device)
-        scales = torch.empty((m, n // 64), dtype=torch.uint8, device=a_codes.device)
-    _call("fp4dit_gemm_fp4_epilogue_swiglu", m, n, k, _ptr(a_codes), _ptr(a_scales), _ptr(b_codes),
-          _ptr(b_scales), _ptr(h), _dtype_code(h.dtype) if h is not None else F32, _ptr(codes), _ptr(scales),
-          _stream())
-    return h, codes, scales
+def gemm_fp4_epilogue_swiglu(a: MxTensor, b: MxTensor, out_dtype=torch.bfloat16, requant=False, out=None,
+                             out_mx: Optional[MxTensor] = None):
+    """SwiGLU over an interleaved weight.  Returns (h or None, MxTensor or None):
+    h [M, N/2] when out_dtype (or `out`) is given, its tiled MXFP4 encoding
+    when requant is set (into `out_mx` if given)."""
+    m, n, k = _gemm_shapes(a, b)
+    h = out
+    if h is None and out_dtype is not None:
+        h = torch.empty((m, n // 2), dtype=out_dtype, device=a.codes.device)
+    mx = None
+    if requant:
+        mx = out_mx if out_mx is not None else mx_empty(m, n // 2, "tiled", a.codes.device)
+    _call("fp4dit_gemm_fp4_epilogue_swiglu", m, n, k, _ptr(a.codes), _ptr(a.scales), _ptr(b.codes),
+          _ptr(b.scales), _ptr(h), _dtype_code(h.dtype) if h is not None else F32,
+          _ptr(mx.codes) if mx else None, _ptr(mx.scales) if mx else None, _stream())
+    return h, mx

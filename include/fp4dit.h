@@ -10,15 +10,31 @@
  *   synchronises: each call enqueues its kernels on `stream` (the null stream
  *   is allowed) and returns.  Outputs are valid once the stream reaches them.
  * - All matrices are dense and row-major, with no leading-dimension padding.
- * - MXFP4 tensors are a pair (codes, scales):
- *     codes  uint8 [rows][cols/2]  two e2m1 codes per byte, element 2j in the
- *                                  low nibble; code = sign<<3 | exp<<1 | mant
- *                                  with exponent bias 1 (magnitudes 0, 0.5, 1,
- *                                  1.5, 2, 3, 4, 6);
- *     scales uint8 [rows][cols/32] e8m0 power-of-two scale 2^(byte - 127) of
- *                                  each run of 32 consecutive elements of a row.
- *   The GEMM operands both block along K: A is [M][K], B (the packed weight)
- *   is [N][K].
+ * - MXFP4 tensors are a pair (codes, scales): 4-bit e2m1 codes
+ *   (code = sign<<3 | exp<<1 | mant, exponent bias 1: magnitudes 0, 0.5, 1,
+ *   1.5, 2, 3, 4, 6) and one e8m0 scale byte 2^(byte - 127) for each run of
+ *   32 consecutive elements of a row.  Two byte layouts (fp4dit_layout):
+ *
+ *   FP4DIT_MX_ROWMAJOR  codes  uint8 [rows][cols/2], element 2j of a row in
+ *                              the low nibble of byte j;
+ *                       scales uint8 [rows][cols/32].
+ *   FP4DIT_MX_TILED     the layout the GEMM reads (cols % 128 == 0):
+ *                       codes in 128-byte tiles of 2 rows x 128 elements;
+ *                       tile (r/2, k/128) at byte ((r/2)*(cols/128) + k/128)*128,
+ *                       inside it row r%2 at +64*(r%2) and elements k%128
+ *                       packed as above (element pair (k, k+1) at byte
+ *                       (k%128)/2, k in the low nibble).  Buffer:
+ *                       round_up(rows, 2) * cols/2 bytes.
+ *                       scales in 128-byte tiles of 32 rows x 4 blocks: the
+ *                       byte of (row r, block b) is at
+ *                       ((r/32)*(cols/128) + b/4)*128 + (r%32)*4 + b%4.
+ *                       Buffer: round_up(rows, 32) * cols/32 bytes.
+ *   One tiled scale tile is exactly what a 32x32x64 scaled MFMA operand
+ *   needs per 32 rows and 128 K-elements, and one code tile feeds two rows
+ *   of a 128-deep K stage, so the GEMM fetches whole cache lines.  Padding
+ *   rows are never read.
+ *   The GEMM operands A (activations, [M][K]) and B (packed weight, [N][K])
+ *   are both MX_TILED, blocked along K.
  * - Arguments are checked on the host before anything is enqueued.  A
  *   status other than FP4DIT_OK means nothing was enqueued, except
  *   FP4DIT_E_LAUNCH, which reports a failed kernel launch.  No exception
@@ -59,6 +75,11 @@ typedef enum fp4dit_dtype {
     FP4DIT_BF16 = 1           /* bfloat16 (uint16 bit patterns)                 */
 } fp4dit_dtype;
 
+typedef enum fp4dit_layout {
+    FP4DIT_MX_ROWMAJOR = 0,   /* plain row-major codes and scales               */
+    FP4DIT_MX_TILED = 1       /* 128-byte MFMA tiles (see above); GEMM operands */
+} fp4dit_layout;
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* fp4dit_status_string(fp4dit_status s);
 
@@ -68,7 +89,8 @@ const char* fp4dit_status_string(fp4dit_status s);
  * FP4 element); KroQuant, "Deep analysis" (W4A4 in MXFP4).
  *
  * x      [rows][cols] of x_dtype (F32 or BF16), 16-byte aligned.
- * codes  [rows][cols/2], 16-byte aligned;  scales [rows][cols/32].
+ * codes, scales in `layout` (16-byte aligned codes); MX_TILED needs
+ * cols % 128 == 0.
  * Per 32-element block: amax = max |x|; shared exponent
  * s = clamp(floor(log2 amax) - 2, -127, 127) (s = -127 for an all-zero
  * block); scale byte = s + 127; every element is x / 2^s rounded to the
@@ -79,7 +101,7 @@ const char* fp4dit_status_string(fp4dit_status s);
  */
 fp4dit_status fp4dit_quantize_mxfp4(const void* x, fp4dit_dtype x_dtype,
                                     int64_t rows, int64_t cols,
-                                    uint8_t* codes, uint8_t* scales,
+                                    uint8_t* codes, uint8_t* scales, fp4dit_layout layout,
                                     hipStream_t stream);
 
 /*
@@ -97,7 +119,8 @@ fp4dit_status fp4dit_quantize_mxfp4(const void* x, fp4dit_dtype x_dtype,
  * y       NULL, or [rows][cols] of y_dtype (F32 or BF16, 16-byte aligned):
  *         the fp32 product, stored (BF16: round to nearest even).
  * codes, scales  both NULL, or both set: MXFP4 of the fp32 product exactly as
- *         fp4dit_quantize_mxfp4 would encode it (x never round-trips HBM).
+ *         fp4dit_quantize_mxfp4 would encode it, in `layout` (x never
+ *         round-trips HBM).
  * At least one of y / codes must be set.  Products are formed from bf16
  * operands (an F32 x is rounded to bf16 first) and summed in fp32.
  * Requires cols % 32 == 0.
@@ -106,7 +129,7 @@ fp4dit_status fp4dit_block_transform(const void* x, fp4dit_dtype x_dtype,
                                      int64_t rows, int64_t cols,
                                      const uint16_t* t_bf16, int64_t n_t,
                                      void* y, fp4dit_dtype y_dtype,
-                                     uint8_t* codes, uint8_t* scales,
+                                     uint8_t* codes, uint8_t* scales, fp4dit_layout layout,
                                      hipStream_t stream);
 
 /*
@@ -131,7 +154,8 @@ fp4dit_status fp4dit_fold_inverse_transform(const float* w, int64_t K, int64_t N
  * weight quantisation for inference, QAD section).
  *
  * w      [K][N] of w_dtype (F32 or BF16), logical y = x . W.
- * interleave_group  0: no permutation, codes [N][K/2], scales [N][K/32].
+ * codes, scales: the [N][K] MXFP4 weight in `layout` (MX_TILED for the GEMM).
+ * interleave_group  0: no permutation.
  *        g > 0: SwiGLU weight (fal, "Fusing gated SiLU"): w holds
  *        [gate | up], N/2 columns each; physical column p takes logical
  *        output j = (p / 2g) * g + p % g from the up half if (p / g) is odd,
@@ -143,7 +167,7 @@ fp4dit_status fp4dit_fold_inverse_transform(const float* w, int64_t K, int64_t N
  */
 fp4dit_status fp4dit_pack_weight(const void* w, fp4dit_dtype w_dtype,
                                  int64_t K, int64_t N, int32_t interleave_group,
-                                 uint8_t* codes, uint8_t* scales,
+                                 uint8_t* codes, uint8_t* scales, fp4dit_layout layout,
                                  hipStream_t stream);
 
 /* Interleave group size g the SwiGLU epilogue expects (see fp4dit_pack_weight). */
@@ -155,9 +179,10 @@ int32_t fp4dit_swiglu_interleave_group(void);
  * fp32 accumulators; the epilogue runs before the one store to HBM):
  *     C[m][n] = sum_k D(A)[m][k] * D(B)[n][k]
  * with D() the exact MXFP4 value, scaled FP4 matrix-core products and fp32
- * accumulation.  Shapes: a_codes [M][K/2], a_scales [M][K/32], b_codes
- * [N][K/2], b_scales [N][K/32]; every codes pointer 16-byte aligned, every
- * scales pointer 4-byte aligned.  Requires K % 256 == 0 and K > 0,
+ * accumulation.  A = (a_codes, a_scales) is [M][K] and B = (b_codes,
+ * b_scales) is [N][K], both in the FP4DIT_MX_TILED layout (buffers padded
+ * as stated there); every codes pointer 16-byte aligned, every scales
+ * pointer 4-byte aligned.  Requires K % 256 == 0 and K > 0,
  * N % 256 == 0 and N > 0, and M*K/2 and N*K/2 below 2^31 bytes; M >= 0 is
  * otherwise arbitrary (a ragged last token tile is masked).
  */
@@ -199,8 +224,9 @@ fp4dit_status fp4dit_gemm_fp4_epilogue_rmsnorm_head(int64_t M, int64_t N, int64_
  *     h[m][j] = silu(gate[m][j]) * up[m][j],  silu(z) = z / (1 + exp(-z)).
  * out        NULL, or [M][N/2] of out_dtype (16-byte aligned).
  * out_codes, out_scales  both NULL, or both set: MXFP4 re-quantisation of
- *            the fp32 h along its columns ([M][N/4] codes, 16-byte aligned,
- *            and [M][N/64] scales), encoded as fp4dit_quantize_mxfp4 does.
+ *            the fp32 h [M][N/2] along its columns, in the MX_TILED layout
+ *            (ready to be the A operand of the next GEMM; codes 16-byte
+ *            aligned), encoded as fp4dit_quantize_mxfp4 does.
  * At least one output must be set.
  */
 fp4dit_status fp4dit_gemm_fp4_epilogue_swiglu(int64_t M, int64_t N, int64_t K,

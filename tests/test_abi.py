@@ -17,6 +17,7 @@ HEADER = os.path.join(ROOT, "include", "fp4dit.h")
 
 OK, E_NULL, E_SHAPE, E_ALIGN, E_UNSUP = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
+ROWMAJOR, TILED = 0, 1
 P = 0x10000          # a fake, 64 KiB-aligned "device" address: never dereferenced
 P_ODD = 0x10001
 
@@ -50,14 +51,16 @@ def test_status_strings_and_group(L):
 
 def test_quantize_validation(L):
     q = L.fp4dit_quantize_mxfp4
-    assert q(P, F32, 4, 48, P, P, None) == E_SHAPE           # cols % 32
-    assert q(P, F32, -1, 64, P, P, None) == E_SHAPE
-    assert q(P, 7, 4, 64, P, P, None) == E_UNSUP             # dtype
-    assert q(None, BF16, 4, 64, P, P, None) == E_NULL
-    assert q(P, BF16, 4, 64, None, P, None) == E_NULL
-    assert q(P_ODD, BF16, 4, 64, P, P, None) == E_ALIGN
-    assert q(P, BF16, 4, 64, P_ODD, P, None) == E_ALIGN
-    assert q(None, BF16, 0, 64, None, None, None) == OK       # empty: nothing to do
+    assert q(P, F32, 4, 48, P, P, ROWMAJOR, None) == E_SHAPE           # cols % 32
+    assert q(P, F32, 4, 96, P, P, TILED, None) == E_SHAPE              # tiled: cols % 128
+    assert q(P, F32, -1, 64, P, P, ROWMAJOR, None) == E_SHAPE
+    assert q(P, 7, 4, 64, P, P, ROWMAJOR, None) == E_UNSUP             # dtype
+    assert q(P, F32, 4, 128, P, P, 5, None) == E_UNSUP                 # layout
+    assert q(None, BF16, 4, 64, P, P, ROWMAJOR, None) == E_NULL
+    assert q(P, BF16, 4, 64, None, P, ROWMAJOR, None) == E_NULL
+    assert q(P_ODD, BF16, 4, 64, P, P, ROWMAJOR, None) == E_ALIGN
+    assert q(P, BF16, 4, 64, P_ODD, P, ROWMAJOR, None) == E_ALIGN
+    assert q(None, BF16, 0, 64, None, None, ROWMAJOR, None) == OK       # empty: nothing to do
 
 
 def test_gemm_validation(L):
@@ -97,14 +100,16 @@ def test_swiglu_validation(L):
 
 def test_transform_pack_fold_validation(L):
     bt = L.fp4dit_block_transform
-    assert bt(P, BF16, 8, 96, P, 2, P, F32, None, None, None) == E_SHAPE   # n_t not 1 or cols/32
-    assert bt(P, BF16, 8, 96, P, 3, None, F32, None, None, None) == E_NULL  # no output
-    assert bt(P, BF16, 8, 96, P, 1, None, F32, P, None, None) == E_UNSUP   # codes without scales
-    assert bt(P, BF16, 8, 80, P, 1, P, F32, None, None, None) == E_SHAPE
+    assert bt(P, BF16, 8, 96, P, 2, P, F32, None, None, TILED, None) == E_SHAPE   # n_t not 1 or cols/32
+    assert bt(P, BF16, 8, 96, P, 3, None, F32, None, None, TILED, None) == E_NULL  # no output
+    assert bt(P, BF16, 8, 96, P, 1, None, F32, P, None, TILED, None) == E_UNSUP   # codes without scales
+    assert bt(P, BF16, 8, 80, P, 1, P, F32, None, None, TILED, None) == E_SHAPE
+    assert bt(P, BF16, 8, 96, P, 1, None, F32, P, P, TILED, None) == E_SHAPE      # tiled: cols % 128
     pw = L.fp4dit_pack_weight
-    assert pw(P, F32, 64, 96, 32, P, P, None) == E_SHAPE                   # N % 2g
-    assert pw(P, F32, 48, 64, 0, P, P, None) == E_SHAPE                    # K % 32
-    assert pw(P, F32, 64, 64, -1, P, P, None) == E_UNSUP
+    assert pw(P, F32, 64, 96, 32, P, P, ROWMAJOR, None) == E_SHAPE                # N % 2g
+    assert pw(P, F32, 48, 64, 0, P, P, ROWMAJOR, None) == E_SHAPE                 # K % 32
+    assert pw(P, F32, 64, 64, 0, P, P, TILED, None) == E_SHAPE                    # tiled: K % 128
+    assert pw(P, F32, 64, 64, -1, P, P, ROWMAJOR, None) == E_UNSUP
     fo = L.fp4dit_fold_inverse_transform
     assert fo(P, 64, 16, P, 3, P + 64, None) == E_SHAPE
     assert fo(P, 64, 16, P, 2, P, None) == E_UNSUP                          # aliasing

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import layout
 import parity
 from gpu_util import announce, dev, dev_u8, host
 from fp4_diffusion_transformer_amd import ops
@@ -29,8 +30,15 @@ def _operands(rng, m, n, k, spread=True):
     return ac, as_, bc, bs
 
 
+def _mx(codes, scales):
+    """Oracle codes (unpacked, row-major) -> tiled MxTensor on the device."""
+    rows, cols = codes.shape
+    return ops.MxTensor(dev_u8(layout.tile_codes(mxfp4.pack_codes(codes))), dev_u8(layout.tile_scales(scales)),
+                        rows, cols, "tiled")
+
+
 def _dev_ops(ac, as_, bc, bs):
-    return (dev_u8(mxfp4.pack_codes(ac)), dev_u8(as_), dev_u8(mxfp4.pack_codes(bc)), dev_u8(bs))
+    return _mx(ac, as_), _mx(bc, bs)
 
 
 def test_exact_on_representable_inputs():
@@ -136,8 +144,8 @@ def test_swiglu_values(m, out_dtype):
     rng = np.random.default_rng(11 + m)
     operands, h_ref = _swiglu_operands(rng, m, 384, 512)
     announce("gemm swiglu", m, out_dtype)
-    h, codes, scales = ops.gemm_fp4_epilogue_swiglu(*_dev_ops(*operands), out_dtype=out_dtype, requant=False)
-    assert codes is None
+    h, mx = ops.gemm_fp4_epilogue_swiglu(*_dev_ops(*operands), out_dtype=out_dtype, requant=False)
+    assert mx is None
     tol = parity.TOL_F32 if out_dtype == torch.float32 else parity.TOL_BF16
     parity.assert_close(host(h), h_ref, tol, what="swiglu")
 
@@ -147,12 +155,13 @@ def test_swiglu_requant(with_bf16):
     rng = np.random.default_rng(21)
     operands, h_ref = _swiglu_operands(rng, 300, 512, 768)
     announce("gemm swiglu requant", with_bf16)
-    h, codes, scales = ops.gemm_fp4_epilogue_swiglu(*_dev_ops(*operands),
-                                                    out_dtype=torch.bfloat16 if with_bf16 else None,
-                                                    requant=True)
+    h, mx = ops.gemm_fp4_epilogue_swiglu(*_dev_ops(*operands), out_dtype=torch.bfloat16 if with_bf16 else None,
+                                         requant=True)
     if with_bf16:
         parity.assert_close(host(h), h_ref, parity.TOL_BF16, what="swiglu bf16 + requant")
     else:
         assert h is None
-    exc_codes, exc_blocks = parity.assert_codes_banded(host(codes), host(scales), h_ref, "swiglu requant")
+    codes = layout.untile_codes(host(mx.codes), mx.rows, mx.cols)
+    scales = layout.untile_scales(host(mx.scales), mx.rows, mx.cols)
+    exc_codes, exc_blocks = parity.assert_codes_banded(codes, scales, h_ref, "swiglu requant")
     assert exc_codes <= 0.001 * h_ref.size

@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import golden_io
+import layout
 import parity
 from gpu_util import announce, dev, dev_u8, host
 from fp4_diffusion_transformer_amd import ops, workloads
@@ -19,11 +20,15 @@ from oracle import mxfp4
 pytestmark = pytest.mark.gpu
 
 
-def _quant_both(x64, dtype):
-    announce("quantize", x64.shape, dtype)
-    codes, scales = ops.quantize_mxfp4(dev(x64, dtype))
+def _quant_both(x64, dtype, lay="rowmajor"):
+    """GPU quantisation, returned as row-major packed codes and scales."""
+    announce("quantize", x64.shape, dtype, lay)
+    mx = ops.quantize_mxfp4(dev(x64, dtype), layout=lay)
     torch.cuda.synchronize()
-    return host(codes), host(scales)
+    rows, cols = x64.shape
+    if lay == "tiled":
+        return layout.untile_codes(host(mx.codes), rows, cols), layout.untile_scales(host(mx.scales), rows, cols)
+    return host(mx.codes), host(mx.scales)
 
 
 def test_hand_worked_blocks_fp32_and_bf16():
@@ -51,13 +56,15 @@ def test_every_bf16_value():
     x = np.concatenate(rows)
     x = x[: (len(x) // 8) * 8].reshape(-1, 256)   # 8 blocks per row
     rc, rs = mxfp4.quantize(x)
-    gc, gs = _quant_both(x, torch.bfloat16)
+    gc, gs = _quant_both(x, torch.bfloat16, "tiled")
     parity.assert_codes_exact(gc, gs, rc, rs, "all bf16")
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("rows,cols", [(1, 32), (3, 96), (257, 3072), (1000, 512)])
-def test_random_with_outliers(dtype, rows, cols):
+@pytest.mark.parametrize("rows,cols,lay", [(1, 32, "rowmajor"), (3, 96, "rowmajor"), (257, 3072, "rowmajor"),
+                                           (1000, 512, "rowmajor"), (1, 128, "tiled"), (33, 384, "tiled"),
+                                           (257, 3072, "tiled")])
+def test_random_with_outliers(dtype, rows, cols, lay):
     rng = np.random.default_rng(rows * 7 + cols)
     x = rng.standard_normal((rows, cols)) * 2.0 ** rng.integers(-30, 30, (rows, 1))
     x[:, rng.choice(cols, max(1, cols // 200), replace=False)] *= 20
@@ -67,34 +74,42 @@ def test_random_with_outliers(dtype, rows, cols):
         x = workloads.to_bf16_values(x)
     x = x.astype(np.float64)
     rc, rs = mxfp4.quantize(x)
-    gc, gs = _quant_both(x, dtype)
-    parity.assert_codes_exact(gc, gs, rc, rs, "random %s" % dtype)
+    gc, gs = _quant_both(x, dtype, lay)
+    parity.assert_codes_exact(gc, gs, rc, rs, "random %s %s" % (dtype, lay))
 
 
 def test_empty_rows_is_a_no_op():
-    x = torch.zeros((0, 64), device="cuda", dtype=torch.bfloat16)
-    codes, scales = ops.quantize_mxfp4(x)
-    assert codes.shape == (0, 32) and scales.shape == (0, 2)
+    x = torch.zeros((0, 128), device="cuda", dtype=torch.bfloat16)
+    mx = ops.quantize_mxfp4(x)
+    assert mx.rows == 0 and mx.codes.shape == (0, 64) and mx.scales.shape == (0, 4)
 
 
 def test_workload_activations_bit_exact():
     w = workloads.qkv_hd128(rows=4096)
     rc, rs = mxfp4.quantize(w.x.astype(np.float64))
-    gc, gs = _quant_both(w.x.astype(np.float64), torch.bfloat16)
+    gc, gs = _quant_both(w.x.astype(np.float64), torch.bfloat16, "tiled")
     parity.assert_codes_exact(gc, gs, rc, rs, "qkv activations 4096x3072")
 
 
+def _mx_host(mx):
+    if mx.layout == "tiled":
+        return (layout.untile_codes(host(mx.codes), mx.rows, mx.cols),
+                layout.untile_scales(host(mx.scales), mx.rows, mx.cols))
+    return host(mx.codes), host(mx.scales)
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_pack_weight_plain(dtype):
+@pytest.mark.parametrize("lay", ["rowmajor", "tiled"])
+def test_pack_weight_plain(dtype, lay):
     rng = np.random.default_rng(5)
     k, n = 512, 320
     w = rng.standard_normal((k, n)).astype(np.float32) / 20
     if dtype == torch.bfloat16:
         w = workloads.to_bf16_values(w)
-    announce("pack_weight", k, n, dtype)
-    gc, gs = ops.pack_weight(dev(w, dtype))
+    announce("pack_weight", k, n, dtype, lay)
+    gc, gs = _mx_host(ops.pack_weight(dev(w, dtype), layout=lay))
     rc, rs = mxfp4.quantize(w.astype(np.float64).T)
-    parity.assert_codes_exact(host(gc), host(gs), rc, rs, "pack plain")
+    parity.assert_codes_exact(gc, gs, rc, rs, "pack plain")
 
 
 def test_pack_weight_swiglu_interleave():
@@ -104,7 +119,7 @@ def test_pack_weight_swiglu_interleave():
     wu = rng.standard_normal((k, n_half)).astype(np.float32) * 3
     g = ops.swiglu_interleave_group()
     announce("pack_weight swiglu", k, 2 * n_half, g)
-    gc, gs = ops.pack_weight(dev(np.concatenate([wg, wu], axis=1), torch.float32), interleave_group=g)
+    gc, gs = _mx_host(ops.pack_weight(dev(np.concatenate([wg, wu], axis=1), torch.float32), interleave_group=g))
     phys = ogemm.interleave_weight(wg, wu, g)
     rc, rs = mxfp4.quantize(phys.astype(np.float64).T)
-    parity.assert_codes_exact(host(gc), host(gs), rc, rs, "pack interleaved")
+    parity.assert_codes_exact(gc, gs, rc, rs, "pack interleaved")

@@ -4,6 +4,7 @@ import numpy as np
 import pytest
 import torch
 
+import layout
 import parity
 from gpu_util import announce, dev, host
 from fp4_diffusion_transformer_amd import ops, workloads
@@ -16,9 +17,18 @@ def _t(n_t, seed):
     return workloads.transforms(seed, n_t)
 
 
-@pytest.mark.parametrize("rows,cols,n_t", [(300, 512, 16), (300, 512, 1), (1, 96, 3), (129, 160, 5)])
+def _codes_host(mx):
+    if mx.layout == "tiled":
+        return (layout.untile_codes(host(mx.codes), mx.rows, mx.cols),
+                layout.untile_scales(host(mx.scales), mx.rows, mx.cols))
+    return host(mx.codes), host(mx.scales)
+
+
+@pytest.mark.parametrize("rows,cols,n_t,lay", [(300, 512, 16, "tiled"), (300, 512, 1, "rowmajor"),
+                                               (1, 96, 3, "rowmajor"), (129, 160, 5, "rowmajor"),
+                                               (129, 384, 12, "tiled")])
 @pytest.mark.parametrize("x_dtype", [torch.bfloat16, torch.float32])
-def test_transform_values(rows, cols, n_t, x_dtype):
+def test_transform_values(rows, cols, n_t, lay, x_dtype):
     rng = np.random.default_rng(rows + cols + n_t)
     x = rng.standard_normal((rows, cols)).astype(np.float32)
     x[:, rng.choice(cols, 2, replace=False)] *= 20
@@ -27,10 +37,11 @@ def test_transform_values(rows, cols, n_t, x_dtype):
     ref = transform.block_transform(xb.astype(np.float64), t.astype(np.float64))
     announce("block_transform values", rows, cols, n_t, x_dtype)
     xin = xb if x_dtype == torch.bfloat16 else x
-    y, codes, scales = ops.block_transform(dev(xin, x_dtype), dev(t, torch.bfloat16), y_dtype=torch.float32,
-                                           quantize=True)
+    y, mx = ops.block_transform(dev(xin, x_dtype), dev(t, torch.bfloat16), y_dtype=torch.float32, quantize=True,
+                                layout=lay)
     parity.assert_close(host(y), ref, 1e-5, what="transform fp32 y")
-    exc, blk = parity.assert_codes_banded(host(codes), host(scales), ref, "transform codes")
+    codes, scales = _codes_host(mx)
+    exc, blk = parity.assert_codes_banded(codes, scales, ref, "transform codes")
     assert exc <= 0.001 * ref.size
 
 
@@ -40,9 +51,9 @@ def test_transform_bf16_y_only():
     t = _t(8, 9)
     ref = transform.block_transform(x.astype(np.float64), t.astype(np.float64))
     announce("block_transform bf16 y")
-    y, codes, scales = ops.block_transform(dev(x, torch.bfloat16), dev(t, torch.bfloat16),
-                                           y_dtype=torch.bfloat16, quantize=False)
-    assert codes is None
+    y, mx = ops.block_transform(dev(x, torch.bfloat16), dev(t, torch.bfloat16), y_dtype=torch.bfloat16,
+                                quantize=False)
+    assert mx is None
     parity.assert_close(host(y), ref, parity.TOL_BF16, what="transform bf16 y")
 
 
@@ -54,8 +65,9 @@ def test_identity_transform_equals_plain_quantize():
     t = np.broadcast_to(np.eye(32, dtype=np.float32), (1, 32, 32)).copy()
     rc, rs = mxfp4.quantize(x)
     announce("block_transform identity")
-    _, codes, scales = ops.block_transform(dev(x, torch.bfloat16), dev(t, torch.bfloat16), quantize=True)
-    parity.assert_codes_exact(host(codes), host(scales), rc, rs, "identity transform")
+    _, mx = ops.block_transform(dev(x, torch.bfloat16), dev(t, torch.bfloat16), quantize=True)
+    codes, scales = _codes_host(mx)
+    parity.assert_codes_exact(codes, scales, rc, rs, "identity transform")
 
 
 def test_fold_inverse():
