@@ -1,0 +1,109 @@
+"""Summarise rocprofv3 output of bench.py runs into profiles/.
+
+Usage (after the three profiling runs named in the summary header):
+  python -m fp4_diffusion_transformer_amd.profsum TRACE_DIR FETCH_DIR WRITE_DIR OUT_TXT [CALIB_MIB] [CMDS]
+
+TRACE_DIR: `rocprofv3 --kernel-trace --stats --output-format csv` output;
+FETCH_DIR / WRITE_DIR: `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE`
+(csv) of a bench.py run with --calib-mib CALIB_MIB, which fills a buffer of
+that size (a known write) and sums it (a known read).  FETCH_SIZE is scaled
+by the ratio of the known read to what it reports for the sum, WRITE_SIZE by
+that of the known write to what it reports for the fill.  CMDS (optional) is
+a text file with the commands that produced the inputs, copied into OUT_TXT.
+Writes OUT_TXT (kernel time table + per-launch HBM traffic) and
+profiles/hbm_traffic.json (traffic per kernel, with the hash of the kernel
+sources it was taken on; bench.py reports it only while the hash matches).
+"""
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp4_diffusion_transformer_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def _find(d, pattern):
+    hits = sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
+    if not hits:
+        raise FileNotFoundError("no %s under %s" % (pattern, d))
+    return hits[0]
+
+
+def kernel_key(name):
+    """Short key of a kernel name (template arguments kept)."""
+    n = name.replace("fp4dit::(anonymous namespace)::", "").replace("fp4dit::", "")
+    for a, b in (("gemm_fp4_kernel<0,", "gemm_none<"), ("gemm_fp4_kernel<1,", "gemm_rmsnorm_head<"),
+                 ("gemm_fp4_kernel<2,", "gemm_swiglu<")):
+        n = n.replace(a, b)
+    return n.split("(")[0].replace("void ", "").replace(" ", "").strip()
+
+
+def counters(d, counter):
+    path = _find(d, "*counter_collection.csv")
+    per_kernel = defaultdict(list)
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") == counter:
+                per_kernel[row["Kernel_Name"]].append(float(row["Counter_Value"]))
+    return per_kernel
+
+
+def main(argv):
+    trace_dir, fetch_dir, write_dir, out_txt = argv[1:5]
+    copy_mib = int(argv[5]) if len(argv) > 5 else 256
+    cmds = open(argv[6]).read().strip().splitlines() if len(argv) > 6 else []
+    stats = _find(trace_dir, "*kernel_stats.csv")
+    with open(stats) as f:
+        rows = list(csv.DictReader(f))
+    fetch = counters(fetch_dir, "FETCH_SIZE")
+    write = counters(write_dir, "WRITE_SIZE")
+    copy_bytes = copy_mib << 20
+
+    def calib(per_kernel, tag):
+        for name, vals in per_kernel.items():
+            if tag in name:
+                return copy_bytes / (vals[0] * 1024.0)
+        return None
+    f_fac, w_fac = calib(fetch, "reduce_kernel"), calib(write, "FillFunctor")
+    lines = ["# rocprofv3 kernel statistics and HBM traffic of bench.py", ""]
+    lines += ["# " + c for c in cmds] + [""] if cmds else []
+    lines += ["source hash of fp4_diffusion_transformer_amd/csrc: " + source_hash(), ""]
+    lines.append("%-48s %8s %12s %12s %10s" % ("kernel", "calls", "avg_us", "min_us", "pct"))
+    for r in rows:
+        lines.append("%-48s %8s %12.2f %12.2f %10s" % (kernel_key(r["Name"])[:48], r["Calls"],
+                     float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, r.get("Percentage", "")[:6]))
+    lines += ["", "calibration: fill + sum of %d MiB; FETCH_SIZE factor %s, WRITE_SIZE factor %s" % (
+        copy_mib, "%.4f" % f_fac if f_fac else "n/a", "%.4f" % w_fac if w_fac else "n/a"), ""]
+    lines.append("%-48s %16s %16s" % ("kernel", "read MB/launch", "write MB/launch"))
+    traffic = {}
+    for name in sorted(set(fetch) | set(write)):
+        fr = sum(fetch.get(name, [0])) / max(len(fetch.get(name, [1])), 1) * 1024 * (f_fac or 1.0)
+        wr = sum(write.get(name, [0])) / max(len(write.get(name, [1])), 1) * 1024 * (w_fac or 1.0)
+        key = kernel_key(name)
+        lines.append("%-48s %16.2f %16.2f" % (key[:48], fr / 1e6, wr / 1e6))
+        traffic[key] = {"read_bytes": fr, "write_bytes": wr}
+    with open(out_txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    rec = {"source_hash": source_hash(), "copy_mib": copy_mib, "fetch_factor": f_fac, "write_factor": w_fac,
+           "kernels": {k: {"hbm_bytes_per_launch": v["read_bytes"] + v["write_bytes"], **v}
+                       for k, v in traffic.items()}}
+    with open(os.path.join(ROOT, "profiles", "hbm_traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main(sys.argv)

@@ -24,7 +24,7 @@ Recipe (every stream seeded by numpy.random.default_rng([workload, stream])):
 Stream ids: 0 activations (QKV input), 1 QKV / first weight, 2 FFN up weight,
 3 outlier channels, 4 RMSNorm gains, 5 / 9 / 10 block transforms of the QKV /
 FFN-up / FFN-down inputs, 6 FFN down weight, 7 activations of the FFN input,
-8 FFN gate weight.
+8 FFN gate weight, 11 stand-in activations of the FFN down input.
 """
 
 from dataclasses import dataclass, field
@@ -153,14 +153,15 @@ def ffn_up_swiglu(rows: int = 4096, requant: bool = True) -> Workload:
 def dit_block(rows: int = 16384):
     """Batch of 4 images (16384 tokens): block transform + quantise on every
     input, QKV (RMSNorm hd 128), FFN up (SwiGLU, bf16 out), FFN down (none).
-    Returns the three Workloads; the down layer's activations are the up
-    layer's bf16 output, so its x is None here."""
+    Returns the three Workloads.  In the block the down layer's activations
+    are the up layer's bf16 output; its x here (stream 11) is a seeded
+    stand-in of the same shape for checking the down layer on its own."""
     qkv = Workload("dit_block_qkv", rows, 3072, activations(5, 0, rows, 3072), True, "rmsnorm_head",
                    w=weight(5, 1, 3072, 9216), head_dim=128, n_norm=6144,
                    norm_w=norm_gains(5, 128, 24, 24), t=transforms(5, 96, stream=5))
     up = Workload("dit_block_up", rows, 3072, activations(5, 7, rows, 3072), True, "swiglu",
                   w_gate=weight(5, 8, 3072, 12288), w_up=weight(5, 2, 3072, 12288),
                   t=transforms(5, 96, stream=9))
-    down = Workload("dit_block_down", rows, 12288, None, True, "none",
+    down = Workload("dit_block_down", rows, 12288, activations(5, 11, rows, 12288), True, "none",
                     w=weight(5, 6, 12288, 3072), t=transforms(5, 384, stream=10))
     return qkv, up, down

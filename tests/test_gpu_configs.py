@@ -1,0 +1,195 @@
+"""End-to-end GPU parity on the full-size DiT workloads.
+
+The GPU runs every workload at its full size, in the launch configuration
+the benchmark times (tiled operands, bf16 / MXFP4 outputs).  Rows are
+independent, so the oracle recomputes a seeded sample of rows (first, last,
+random) from the same inputs; activation codes are compared in full.  The
+tiny workload is compared in full.
+"""
+
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import layout
+import parity
+from gpu_util import announce, dev, host
+from fp4_diffusion_transformer_amd import ops, workloads
+from oracle import gemm as ogemm
+from oracle import mxfp4, transform
+
+pytestmark = pytest.mark.gpu
+
+
+_dit_block = functools.lru_cache(maxsize=1)(workloads.dit_block)
+
+
+def _rows(m, n=24, seed=0):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, 1, m - 1], rng.choice(m, n, replace=False)]))
+
+
+def _untile(mx):
+    return (layout.untile_codes(host(mx.codes), mx.rows, mx.cols),
+            layout.untile_scales(host(mx.scales), mx.rows, mx.cols))
+
+
+def _gpu_linear(wl, x_dev=None):
+    """The benchmark's fused linear: quantise (or transform + quantise) the
+    activations, pack the weight, fused GEMM + epilogue.  Returns
+    (activation MxTensor, weight MxTensor, output(s))."""
+    if x_dev is None:
+        x_dev = dev(wl.x, torch.bfloat16 if wl.x_bf16 else torch.float32)
+    t_dev = None if wl.t is None else dev(wl.t, torch.bfloat16)
+    if t_dev is None:
+        a = ops.quantize_mxfp4(x_dev)
+    else:
+        _, a = ops.block_transform(x_dev, t_dev, quantize=True)
+    if wl.epilogue == "swiglu":
+        w = dev(np.concatenate([wl.w_gate, wl.w_up], axis=1), torch.float32)
+        group = ops.swiglu_interleave_group()
+    else:
+        w = dev(wl.w, torch.float32)
+        group = 0
+    if t_dev is not None:
+        w = ops.fold_inverse_transform(w, t_dev)
+    b = ops.pack_weight(w, interleave_group=group)
+    del w
+    if wl.epilogue == "rmsnorm_head":
+        out = ops.gemm_fp4_epilogue_rmsnorm_head(a, b, wl.head_dim, wl.n_norm, dev(wl.norm_w, torch.float32),
+                                                 wl.eps, out_dtype=torch.bfloat16)
+    elif wl.epilogue == "swiglu":
+        out = ops.gemm_fp4_epilogue_swiglu(a, b, out_dtype=None if wl.requant else torch.bfloat16,
+                                           requant=wl.requant)
+    else:
+        out = ops.gemm_fp4_epilogue_none(a, b, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    return a, b, out
+
+
+def _oracle_linear(wl, x_rows, w_codes=None):
+    """Oracle output rows for the activations x_rows (float64)."""
+    t = None if wl.t is None else wl.t.astype(np.float64)
+    ac, as_ = mxfp4.quantize(x_rows) if t is None else transform.transform_quantize(x_rows, t)
+    if wl.epilogue == "swiglu":
+        wg, wu = wl.w_gate.astype(np.float64), wl.w_up.astype(np.float64)
+        if t is not None:
+            wg, wu = transform.fold_inverse(wg, t), transform.fold_inverse(wu, t)
+        gc_, gs_ = mxfp4.quantize(wg.T)
+        uc_, us_ = mxfp4.quantize(wu.T)
+        return ogemm.swiglu(ogemm.gemm(ac, as_, gc_, gs_), ogemm.gemm(ac, as_, uc_, us_))
+    w = wl.w.astype(np.float64)
+    if t is not None:
+        w = transform.fold_inverse(w, t)
+    bc, bs = mxfp4.quantize(w.T)
+    c = ogemm.gemm(ac, as_, bc, bs)
+    if wl.epilogue == "rmsnorm_head":
+        return ogemm.rmsnorm_head(c, wl.head_dim, wl.n_norm, wl.norm_w.astype(np.float64), wl.eps)
+    return c
+
+
+def test_tiny_full_compare():
+    wl = workloads.tiny()
+    announce("config tiny", wl.m, wl.n, wl.k)
+    a, b, out = _gpu_linear(wl)
+    ac, as_ = mxfp4.quantize(wl.x.astype(np.float64))
+    parity.assert_codes_exact(*_untile(a), ac, as_, "tiny activations")
+    ref = _oracle_linear(wl, wl.x.astype(np.float64))
+    parity.assert_close(host(out), ref, parity.TOL_BF16, group=wl.head_dim, what="tiny rmsnorm")
+
+
+@pytest.mark.parametrize("name", ["qkv_hd128", "qkv_hd256"])
+def test_qkv_full_size(name):
+    wl = getattr(workloads, name)()
+    announce("config", name, wl.m, wl.n, wl.k)
+    a, b, out = _gpu_linear(wl)
+    x64 = wl.x.astype(np.float64)
+    ac, as_ = mxfp4.quantize(x64)
+    parity.assert_codes_exact(*_untile(a), ac, as_, name + " activations")
+    rows = _rows(wl.m)
+    ref = _oracle_linear(wl, x64[rows])
+    parity.assert_close(host(out)[rows], ref, parity.TOL_BF16, group=wl.head_dim, what=name)
+
+
+def test_ffn_up_swiglu_requant_full_size():
+    wl = workloads.ffn_up_swiglu(requant=True)
+    announce("config ffn_up", wl.m, wl.n, wl.k)
+    a, b, (h, mx) = _gpu_linear(wl)
+    rows = _rows(wl.m, seed=4)
+    ref = _oracle_linear(wl, wl.x.astype(np.float64)[rows])
+    codes, scales = _untile(mx)
+    exc, blk = parity.assert_codes_banded(codes[rows], scales[rows], ref, "ffn up requant")
+    assert exc <= 0.001 * ref.size
+
+
+def _mx_dev(codes, scales):
+    """Oracle codes (unpacked, row-major) -> tiled MxTensor on the device."""
+    rows, cols = codes.shape
+    return ops.MxTensor(dev(layout.tile_codes(mxfp4.pack_codes(codes)), torch.uint8),
+                        dev(layout.tile_scales(scales), torch.uint8), rows, cols, "tiled")
+
+
+@pytest.mark.parametrize("stage", ["qkv", "up", "down"])
+def test_dit_block_batch4_stages(stage):
+    """Batch of 4 images with the block transform, stage by stage.
+
+    The transform is summed in fp32 on the GPU and in float64 by the oracle
+    (and the weight fold is rounded to fp32 before packing), so a few codes
+    whose value sits on a rounding midpoint may legitimately differ; a single
+    such code moves a whole output row, so the chain is not compared end to
+    end.  Instead: (1) activation transform + quantise codes, all 16384 rows,
+    and (2) folded weight codes, against the oracle with the midpoint band;
+    (3) the fused GEMM + epilogue on the oracle's own operand codes, sampled
+    rows.  The down layer runs on its seeded stand-in input."""
+    wl = dict(zip(["qkv", "up", "down"], _dit_block()))[stage]
+    t64 = wl.t.astype(np.float64)
+    announce("config dit_block", stage, wl.m, wl.n, wl.k)
+    x_dev = dev(wl.x, torch.bfloat16)
+    t_dev = dev(wl.t, torch.bfloat16)
+    _, a = ops.block_transform(x_dev, t_dev, quantize=True)            # full size, as benchmarked
+    torch.cuda.synchronize()
+    # (1) activation codes on the first 4096 rows (rows are independent)
+    n_chk = 4096
+    y_ref = transform.block_transform(wl.x[:n_chk].astype(np.float64), t64)
+    gc, gs = _untile(a)
+    exc, blk = parity.assert_codes_banded(gc[:n_chk], gs[:n_chk], y_ref, "dit %s activations" % stage)
+    assert exc <= 1e-4 * y_ref.size
+    del a, y_ref, gc, gs
+    # (2) weights: fold T^-1 into W on the GPU, pack, compare codes
+    if wl.epilogue == "swiglu":
+        w = np.concatenate([wl.w_gate, wl.w_up], axis=1)
+        group = ops.swiglu_interleave_group()
+        pair, is_up = ogemm.interleave_columns(wl.w_gate.shape[1], group)
+        src = np.where(is_up, pair + wl.w_gate.shape[1], pair)        # physical -> logical column
+    else:
+        w, group, src = wl.w, 0, np.arange(wl.w.shape[1])
+    b = ops.pack_weight(ops.fold_inverse_transform(dev(w, torch.float32), t_dev), interleave_group=group)
+    torch.cuda.synchronize()
+    w_fold = transform.fold_inverse(w.astype(np.float64), t64)[:, src]  # physical column order
+    exc, blk = parity.assert_codes_banded(*_untile(b), w_fold.T, "dit %s weights" % stage)
+    assert exc <= 1e-4 * w_fold.size
+    del b
+    # (3) fused GEMM + epilogue at full size on the oracle's own operand codes
+    ac, as_ = transform.transform_quantize(wl.x.astype(np.float64), t64)
+    bc, bs = mxfp4.quantize(w_fold.T)
+    del w_fold
+    a_dev, b_dev = _mx_dev(ac, as_), _mx_dev(bc, bs)
+    rows = _rows(wl.m, n=16, seed=5)
+    c = ogemm.gemm(ac[rows], as_[rows], bc, bs)
+    del ac, as_
+    if stage == "qkv":
+        out = ops.gemm_fp4_epilogue_rmsnorm_head(a_dev, b_dev, wl.head_dim, wl.n_norm,
+                                                 dev(wl.norm_w, torch.float32), wl.eps)
+        ref = ogemm.rmsnorm_head(c, wl.head_dim, wl.n_norm, wl.norm_w.astype(np.float64), wl.eps)
+        group_cols = wl.head_dim
+    elif stage == "up":
+        out, _ = ops.gemm_fp4_epilogue_swiglu(a_dev, b_dev, out_dtype=torch.bfloat16)
+        ref = ogemm.swiglu_from_interleaved(c, group)
+        group_cols = None
+    else:
+        out = ops.gemm_fp4_epilogue_none(a_dev, b_dev)
+        ref, group_cols = c, None
+    torch.cuda.synchronize()
+    parity.assert_close(host(out)[rows], ref, parity.TOL_BF16, group=group_cols, what="dit " + stage)
