@@ -276,9 +276,12 @@ def main():
     q_avg = float(np.mean(q_ms))
     Ld, Lq = layers[dom], layers[quant_dom]
     achieved = Ld.flops / (g_avg * 1e-3) / 1e12
-    # kernel instantiation as rocprof names it: epilogue, bf16 output, K-loop remainder
+    # kernel instantiation as rocprof names it: epilogue, bf16 output, LDS ring
+    # depth (4, or 3 when K = 256) and the K stages peeled before its loop
     out_bf16 = Ld.out is not None
-    kernel_key = "gemm_%s<%s,%d>" % (Ld.wl.epilogue, "true" if out_bf16 else "false", (Ld.k // 128 - 2) % 3)
+    kt = Ld.k // 128
+    ring = 4 if kt >= 3 else 3
+    kernel_key = "gemm_%s<%s,%d,%d>" % (Ld.wl.epilogue, "true" if out_bf16 else "false", ring, (kt - ring + 1) % ring)
 
     out = {
         "metric": "fused MXFP4 GEMM+epilogue TFLOPS and % of MXFP4 peak at DiT 1K shapes",

@@ -86,15 +86,18 @@ __device__ __forceinline__ int64_t tiled_scale_off(int64_t r, int64_t b, int64_t
 }
 
 // ---------------------------------------------------------------- bf16 ----
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u | ((u >> 16) & 0x8000u);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+// fp32 -> bf16, round to nearest even, with V_CVT_PK_BF16_F32 (two values per
+// instruction; NaN stays NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    const bf16x2_t v = __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    return pack_bf16x2(f, 0.0f) & 0xFFFFu;
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {

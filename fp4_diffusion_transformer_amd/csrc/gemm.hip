@@ -15,17 +15,21 @@
 //   channels) are the MFMA "A" operand, tokens the "B" operand, so a lane's
 //   16 accumulators of a 32x32 block are 4 runs of 4 consecutive channels of
 //   one token: a per-head sum needs one lane swap (l <-> l^32).
-// * Workgroup tile 256 channels x 128 tokens, 4 waves of 128 x 64 (128 fp32
-//   accumulators per lane).  With 76.5 KiB of LDS and <= 256 registers per
-//   lane two workgroups share a CU, so one workgroup's epilogue overlaps the
-//   other's main loop.
-// * K is staged 128 at a time through a 3-deep LDS ring filled by the
-//   direct-to-LDS global_load_lds_dwordx4 (no VGPR staging); stage kt+2 is in
-//   flight while stage kt is multiplied.  One barrier per stage.  The three
-//   ring slots are distinct __shared__ objects and the K loop is unrolled by
-//   three, so every LDS access names its slot statically: the compiler can
-//   then tell the fragment reads of stage kt+1 from the loads still landing
-//   in stage kt+2 and does not drain all loads before each read.
+// * Workgroup tile 256 channels x 256 tokens, 4 waves of 128 x 128: 256 fp32
+//   accumulators per lane, held in the accumulation registers, so one wave
+//   fills a SIMD's register file and a CU runs one workgroup.  The large wave
+//   tile is what bounds the LDS traffic: per K-step a wave reads 8 KiB of
+//   fragments for 16 MFMAs, and the operands enter LDS once per 256 x 256
+//   tile.  With 64 B of codes per row per 128-K stage, LDS (not HBM, not L2
+//   latency) is the shared resource the main loop has to spare.
+// * K is staged 128 at a time through a kRing-deep LDS ring filled by the
+//   direct-to-LDS global_load_lds_dwordx4 (no VGPR staging); stage
+//   kt + kRing - 1 is in flight while stage kt is multiplied.  One barrier
+//   per stage.  The ring slots are distinct __shared__ objects and the K
+//   loop is unrolled by kRing, so every LDS access names its slot
+//   statically: the compiler then tells the fragment reads of stage kt+1
+//   from the loads still landing in later slots and does not drain all
+//   loads before each read.
 // * LDS rows are 64 B (4 chunks of 16 B, one MX block each).  Chunk c of row
 //   r is stored at c ^ ((r >> 2) & 3): each quarter-wave of a fragment read
 //   (16 lanes = rows 0..15, 16 B each) then covers all 64 banks once.
@@ -35,6 +39,8 @@
 //   the same permutation, so the sum over K is unchanged.
 // * bf16 outputs go through LDS (after the main loop) so that every global
 //   store writes whole row segments.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -42,27 +48,25 @@ namespace fp4dit {
 namespace {
 
 constexpr int kBN = 256;               // channels per workgroup
-constexpr int kBM = 128;               // tokens per workgroup
+constexpr int kBM = 256;               // tokens per workgroup
 constexpr int kBK = 128;               // K elements per LDS stage
-constexpr int kStages = 3;
+constexpr int kRing = 4;               // LDS ring depth (stages)
 constexpr int kRowBytes = kBK / 2;     // 64 bytes of codes per row per stage
 constexpr int kScaleBytes = kBK / 32;  // 4 scale bytes per row per stage
 constexpr int kWCodesOff = 0;
 constexpr int kXCodesOff = kWCodesOff + kBN * kRowBytes;        // 16 KiB
-constexpr int kWScalesOff = kXCodesOff + kBM * kRowBytes;       // +8 KiB
+constexpr int kWScalesOff = kXCodesOff + kBM * kRowBytes;       // +16 KiB
 constexpr int kXScalesOff = kWScalesOff + kBN * kScaleBytes;    // +1 KiB
-// Token scales: wave w loads rows 32w..32w+31 with all 64 lanes (lanes 32..63
-// repeat them), so each wave owns a 256-byte slot whose first half is used.
-constexpr int kStageBytes = kXScalesOff + 4 * 256;              // 26 KiB
-constexpr int kLdsBytes = kStages * kStageBytes;                // 78 KiB
-// Epilogue reuse of the ring: each wave stages 32 tokens x 256 B of bf16 at
-// a time (8 KiB): waves 0..2 in stages 0..2, wave 3 in the second 8 KiB of
-// stage 0; the per-token head sums (1 KiB) sit behind wave 1's region.
-constexpr int kStageOutBytes = 8192;
-constexpr int kRedOff = kStageOutBytes;
-static_assert(2 * kStageOutBytes <= kStageBytes && kRedOff + 2 * kBM * 4 <= kStageBytes,
+constexpr int kStageBytes = kXScalesOff + kBM * kScaleBytes;    // 34 KiB
+// Epilogue use of the one ring slot the next tile's prefetch leaves free:
+// each wave stages 32 tokens x 256 B of bf16 at a time in its own region of
+// 32 padded rows (8.5 KiB); the per-token head sums of a 256-wide head (2 KiB)
+// are exchanged at the start of the slot before any wave stages its rows.
+constexpr int kStageOutBytes = 32 * (16 * 16 + 16);
+constexpr int kRedOff = 0;
+static_assert(4 * kStageOutBytes <= kStageBytes && kRedOff + 2 * kBM * 4 <= kStageBytes,
               "epilogue LDS does not fit");
-constexpr int kDmaPerStage = 8;        // direct-to-LDS instructions per wave per stage
+constexpr int kDmaPerStage = 10;       // direct-to-LDS instructions per wave per stage
 
 enum EpiKind { kEpiNone = 0, kEpiRmsNorm = 1, kEpiSwiglu = 2 };
 
@@ -85,6 +89,15 @@ struct GemmArgs {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Compile-time loop: f(integral_constant<int, I>) for I = B .. E-1.
+template <int B, int E, typename F>
+__host__ __device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>());
+        static_for<B + 1, E>(f);
+    }
+}
+
 // s_waitcnt immediate (gfx9 encoding): vmcnt, expcnt, lgkmcnt.
 constexpr int waitcnt_imm(int vm, int exp, int lgkm) {
     return (vm & 15) | ((exp & 7) << 4) | ((lgkm & 15) << 8) | (((vm >> 4) & 3) << 14);
@@ -92,7 +105,7 @@ constexpr int waitcnt_imm(int vm, int exp, int lgkm) {
 
 // Workgroup barrier of the K loop.  __syncthreads() would add a release
 // fence, which drains every outstanding load -- including the direct-to-LDS
-// loads of stage kt+2 that are meant to stay in flight.  Instead each wave
+// loads of later stages that are meant to stay in flight.  Instead each wave
 // waits explicitly (its stage-kt+1 loads landed: at most VM loads remain;
 // its own LDS reads done) and then meets the others at s_barrier.  The empty
 // asm statements keep the compiler from moving LDS accesses across it.
@@ -104,10 +117,33 @@ __device__ __forceinline__ void ring_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Orders the LDS writes and reads of one wave's lanes (a wave's LDS
+// operations execute in order; this only stops the compiler from moving
+// them).
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+}
+
+// A wave-uniform 32-bit value the compiler may not hoist or fold: LDS
+// destinations derived from it cost one scalar add per load instead of one
+// live scalar register per (ring slot, load).
+__device__ __forceinline__ uint32_t opaque_sgpr(uint32_t x) {
+    asm volatile("" : "+s"(x));
+    return x;
+}
+
+// A per-lane 32-bit value the compiler may not hoist: values derived from
+// it are recomputed where used instead of being kept live (or spilled)
+// across the whole tile loop.
+__device__ __forceinline__ uint32_t opaque_vgpr(uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // Per-lane byte offsets of the direct-to-LDS loads, fixed for the K loop (the
 // stage advances the wave-uniform base pointers instead).
 struct LoadPlan {
-    uint32_t w_code[4], x_code[2];
+    uint32_t w_code[4], x_code[4];
     uint32_t w_scale, x_scale;
 };
 
@@ -121,87 +157,110 @@ __device__ __forceinline__ uint32_t scale_tile_off(uint32_t r, uint32_t kq) {
     return ((r >> 5) * kq) * 128 + (r & 31) * 4;
 }
 
-__device__ __forceinline__ LoadPlan make_plan(const GemmArgs& g, int64_t n0, int64_t m0, int wave, int lane) {
+// Each wave loads 64 of the 256 weight rows and 64 of the 256 token rows:
+// one instruction moves 16 rows x 64 B (lane: row lane/4, 16-byte chunk
+// lane%4, written at its swizzled position), the scale instructions 64 rows
+// x 4 B.
+__device__ __forceinline__ LoadPlan make_plan(int M, int K, int n0, int m0, int wave, int lane_) {
     LoadPlan p;
-    const uint32_t kq = (uint32_t)(g.K / 128);          // K stages (tiles per row pair / row block)
+    const int lane = (int)opaque_vgpr((uint32_t)lane_);
+    const uint32_t kq = (uint32_t)(K / 128);            // K stages (tiles per row pair / row block)
     const int rin = lane >> 2;                          // row within a 16-row group
     const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);  // chunk for physical slot lane & 3
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int row = (wave * 4 + j) * 16 + rin;
         p.w_code[j] = code_tile_off((uint32_t)(n0 + row), kq) + lchunk * 16;
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int row = (wave * 2 + j) * 16 + rin;
-        int64_t xr = m0 + row;
-        xr = xr < g.M ? xr : g.M - 1;                   // ragged token tile: clamp, never stored
+        const int xr = m0 + row < M ? m0 + row : M - 1; // ragged token tile: clamp, never stored
         p.x_code[j] = code_tile_off((uint32_t)xr, kq) + lchunk * 16;
     }
     p.w_scale = scale_tile_off((uint32_t)(n0 + wave * 64 + lane), kq);
-    int64_t xr = m0 + wave * 32 + (lane & 31);          // lanes 32..63 repeat lanes 0..31
-    xr = xr < g.M ? xr : g.M - 1;
+    const int xr = m0 + wave * 64 + lane < M ? m0 + wave * 64 + lane : M - 1;
     p.x_scale = scale_tile_off((uint32_t)xr, kq);
     return p;
 }
 
-// Enqueue the 8 direct-to-LDS loads of K stage kt into `stage` (this wave's share).
-__device__ __forceinline__ void issue_stage(uint8_t* stage, const GemmArgs& g, const LoadPlan& p, int kt,
-                                            int wave, int lane) {
-    const uint8_t* wc = g.b_codes + (int64_t)kt * 128;
-    const uint8_t* xc = g.a_codes + (int64_t)kt * 128;
+// Buffer descriptors of the four operand arrays (scalar registers, set up
+// once): every load of a stage then adds the same scalar offset kt * 128 to
+// its fixed per-lane offset.  The record counts are the arrays' sizes.
+struct Operands {
+    __amdgpu_buffer_rsrc_t wc, xc, ws, xs;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const uint8_t* p, int64_t bytes) {
+    constexpr int kRawDword = 0x00020000;               // untyped 32-bit data format, no swizzle
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), (short)0, (int)bytes, kRawDword);
+}
+
+__device__ __forceinline__ Operands make_operands(const GemmArgs& g) {
+    const int64_t m2 = (g.M + 1) & ~int64_t(1), m32 = (g.M + 31) & ~int64_t(31);
+    Operands o;
+    o.wc = buffer_rsrc(g.b_codes, g.N * (g.K / 2));
+    o.xc = buffer_rsrc(g.a_codes, m2 * (g.K / 2));
+    o.ws = buffer_rsrc(g.b_scales, g.N * (g.K / 32));
+    o.xs = buffer_rsrc(g.a_scales, m32 * (g.K / 32));
+    return o;
+}
+
+// Enqueue the 10 direct-to-LDS loads of K stage kt into `stage` (this wave's
+// share; `wave` is wave-uniform).
+__device__ __forceinline__ void issue_stage(uint8_t* stage, const Operands& o, const LoadPlan& p, int kt,
+                                            int wave) {
+    const uint32_t soff = (uint32_t)kt * 128u;
+    const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(stage);
+    const uint32_t codes = opaque_sgpr(lds0 + wave * 4096);       // this wave's 4 x 1 KiB of W and of X
+    const uint32_t scales = opaque_sgpr(lds0 + wave * 256);       // its 256 B of W and of X scales
+    auto lds = [](uint32_t a) { return (lds_void*)(uintptr_t)a; };
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        __builtin_amdgcn_global_load_lds(wc + p.w_code[j], (lds_void*)(stage + kWCodesOff + (wave * 4 + j) * 1024),
-                                         16, 0, 0);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-        __builtin_amdgcn_global_load_lds(xc + p.x_code[j], (lds_void*)(stage + kXCodesOff + (wave * 2 + j) * 1024),
-                                         16, 0, 0);
-    __builtin_amdgcn_global_load_lds(g.b_scales + (int64_t)kt * 128 + p.w_scale,
-                                     (lds_void*)(stage + kWScalesOff + wave * 256), 4, 0, 0);
-    // 128 token rows of scales: 32 per wave, into the wave's 256-byte slot
-    __builtin_amdgcn_global_load_lds(g.a_scales + (int64_t)kt * 128 + p.x_scale,
-                                     (lds_void*)(stage + kXScalesOff + wave * 256), 4, 0, 0);
+    for (int j = 0; j < 4; ++j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(o.wc, lds(codes + kWCodesOff + j * 1024), 16, p.w_code[j], soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(o.xc, lds(codes + kXCodesOff + j * 1024), 16, p.x_code[j], soff, 0, 0);
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(o.ws, lds(scales + kWScalesOff), 4, p.w_scale, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(o.xs, lds(scales + kXScalesOff), 4, p.x_scale, soff, 0, 0);
 }
 
 struct Frags {
-    v4i w[4], x[2];
+    v4i w[4], x[4];
 };
 
 // Fragment reads of K-step s: lane group h takes MX block 2h + s of the stage.
-__device__ __forceinline__ void read_frags(Frags& f, const uint8_t* stage, int wn, int wm, int r32, int h,
+// The slot pointer gets an opaque zero offset so that its per-lane addresses
+// are formed at each use (one add) rather than kept live for every slot.
+__device__ __forceinline__ void read_frags(Frags& f, const uint8_t* stage_, int wn, int wm, int r32, int h,
                                            int s) {
+    const uint8_t* stage = stage_ + opaque_sgpr(0u);
     const int chunk = ((2 * h + s) ^ ((r32 >> 2) & 3)) * 16;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         f.w[i] = *reinterpret_cast<const v4i*>(stage + kWCodesOff + (wn * 128 + i * 32 + r32) * kRowBytes + chunk);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-        f.x[i] = *reinterpret_cast<const v4i*>(stage + kXCodesOff + (wm * 64 + i * 32 + r32) * kRowBytes + chunk);
+    for (int i = 0; i < 4; ++i)
+        f.x[i] = *reinterpret_cast<const v4i*>(stage + kXCodesOff + (wm * 128 + i * 32 + r32) * kRowBytes + chunk);
 }
 
 // Scale bytes 2h, 2h+1 of every fragment row (byte s serves K-step s),
 // read as the row's whole dword: a 16-bit LDS read here makes the compiler
 // wait for every load still in flight (it cannot tell it apart from the
 // loads landing in the other ring slots), a 32-bit one does not.
-__device__ __forceinline__ void read_scales(uint32_t* wsc, uint32_t* xsc, const uint8_t* stage, int wn, int wm,
+__device__ __forceinline__ void read_scales(uint32_t* wsc, uint32_t* xsc, const uint8_t* stage_, int wn, int wm,
                                             int r32, int h) {
+    const uint8_t* stage = stage_ + opaque_sgpr(0u);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         wsc[i] = *reinterpret_cast<const uint32_t*>(stage + kWScalesOff + (wn * 128 + i * 32 + r32) * kScaleBytes) >> (16 * h);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)   // token row wm*64 + i*32 + r32 sits in slot (2wm + i) at r32*4
-        xsc[i] = *reinterpret_cast<const uint32_t*>(stage + kXScalesOff + (wm * 2 + i) * 256 + r32 * kScaleBytes) >> (16 * h);
+    for (int i = 0; i < 4; ++i)
+        xsc[i] = *reinterpret_cast<const uint32_t*>(stage + kXScalesOff + (wm * 128 + i * 32 + r32) * kScaleBytes) >> (16 * h);
 }
 
 template <int S>
-__device__ __forceinline__ void mfma_step(v16f (&acc)[4][2], const Frags& f, const uint32_t* wsc,
+__device__ __forceinline__ void mfma_step(v16f (&acc)[4][4], const Frags& f, const uint32_t* wsc,
                                           const uint32_t* xsc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < 4; ++j) {
             const v8i a = {f.w[i][0], f.w[i][1], f.w[i][2], f.w[i][3], 0, 0, 0, 0};
             const v8i b = {f.x[j][0], f.x[j][1], f.x[j][2], f.x[j][3], 0, 0, 0, 0};
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 4, 4, S, (int)wsc[i],
@@ -209,47 +268,55 @@ __device__ __forceinline__ void mfma_step(v16f (&acc)[4][2], const Frags& f, con
         }
 }
 
-// Scheduling of one K-step: its 8 MFMAs interleaved with the 6 fragment
-// reads of the next K-step and, in the first K-step of a stage, with the 8
-// direct-to-LDS loads of stage kt+2 (masks: 0x008 MFMA, 0x020 VMEM read,
-// 0x100 DS read).
+// Scheduling of one K-step's 16 MFMAs (masks: 0x008 MFMA, 0x020 VMEM read,
+// 0x100 DS read).  First K-step of a stage: interleaved with the 8 fragment
+// reads of the second and, when loads are issued, the 10 direct-to-LDS loads
+// of a later stage.  Second K-step (after the barrier): interleaved with the
+// 8 scale and 8 fragment reads of the next stage.
+template <bool ISSUE>
 __device__ __forceinline__ void sched_step0() {
-#pragma unroll
-    for (int i = 0; i < 6; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    static_for<0, 8>([&](auto) {
+        if (ISSUE) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    });
+    if (ISSUE) {
+        static_for<0, 2>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        });
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+    } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
 }
 __device__ __forceinline__ void sched_step1() {
-#pragma unroll
-    for (int i = 0; i < 6; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    static_for<0, 16>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    });
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // the 8 scale shifts, once the reads landed
     __builtin_amdgcn_sched_barrier(0);
 }
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z * sigmoid(z), with the hardware exp2 and reciprocal (about
+// 1 ulp each): far inside the fp32 tolerance of the epilogue.
+__device__ __forceinline__ float silu_f(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Map the linear workgroup id to a (token tile, channel tile).  Workgroups
 // are dispatched round-robin over the 8 XCDs; consecutive remapped ids land
 // on one XCD and walk a band of 8 token tiles across the channel tiles, so
 // the workgroups an XCD runs together share operand rows in its L2.
-__device__ __forceinline__ void tile_of(int64_t bid, int64_t nwg, int64_t tiles_n, int64_t tiles_m,
-                                        int64_t& tm, int64_t& tn) {
-    int64_t b = bid;
+__device__ __forceinline__ void tile_of(int bid, int nwg, int tiles_n, int tiles_m, int& tm, int& tn) {
+    int b = bid;
     if ((nwg & 7) == 0) b = (bid & 7) * (nwg >> 3) + (bid >> 3);
-    constexpr int64_t kGroupM = 8;
-    const int64_t per_group = kGroupM * tiles_n;
-    const int64_t group = b / per_group;
-    const int64_t first = group * kGroupM;
-    const int64_t gm = (tiles_m - first) < kGroupM ? (tiles_m - first) : kGroupM;
-    const int64_t in = b - group * per_group;
+    constexpr int kGroupM = 8;
+    const int per_group = kGroupM * tiles_n;
+    const int group = b / per_group;
+    const int first = group * kGroupM;
+    const int gm = (tiles_m - first) < kGroupM ? (tiles_m - first) : kGroupM;
+    const int in = b - group * per_group;
     tm = first + in % gm;
     tn = in / gm;
 }
@@ -257,14 +324,19 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t nwg, int64_t tiles_
 // Store 32 tokens x 8Q bf16 columns of this wave through its LDS region so
 // that every global store writes whole row segments.  vals(q, v) gives the
 // lane's 4 fp32 values of 8-column chunk q (half h) for token tok0 + r32.
-// In LDS, chunk q of token row t sits at q ^ (t % Q) and its two halves are
-// swapped on every other group of Q rows, so both the 8-byte writes and the
-// 16-byte row reads spread over all banks.  Called by all 4 waves together.
+// Token rows sit kRowPad = 16Q + 16 bytes apart: the 16-byte pad rotates
+// consecutive rows by four banks, so both the 8-byte writes (lanes = 32 rows
+// x 2 halves) and the 16-byte row reads are free of bank conflicts, and all
+// accesses of a lane share one base address (immediate offsets).  Only this
+// wave touches `region` (32 * kRowPad bytes).
+template <int Q>
+constexpr int row_pad_bytes() { return Q * 16 + 16; }
+
 template <int Q, typename F>
 __device__ __forceinline__ void store_bf16_half(uint8_t* region, F vals, uint16_t* out, int64_t ld,
                                                 int64_t tok0, int64_t col0, int64_t M, int r32, int h, int lane) {
-    constexpr int kRow = Q * 16;                       // bytes per token row
-    const int t = r32;
+    constexpr int kRowPad = row_pad_bytes<Q>();
+    uint8_t* wbase = region + r32 * kRowPad + h * 8;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         float v[4];
@@ -272,41 +344,39 @@ __device__ __forceinline__ void store_bf16_half(uint8_t* region, F vals, uint16_
         v2u o;
         o[0] = pack_bf16x2(v[0], v[1]);
         o[1] = pack_bf16x2(v[2], v[3]);
-        const int off = t * kRow + ((q ^ (t % Q)) * 16) + ((h ^ ((t / Q) & 1)) * 8);
-        *reinterpret_cast<v2u*>(region + off) = o;
+        *reinterpret_cast<v2u*>(wbase + q * 16) = o;
     }
-    __syncthreads();
+    wave_lds_fence();
     constexpr int kRowsPerInst = 64 / Q;               // Q lanes x 16 B per token row
+    const int q = lane % Q;
+    const uint8_t* rbase = region + (lane / Q) * kRowPad + q * 16;
 #pragma unroll
     for (int it = 0; it < 32 / kRowsPerInst; ++it) {
-        const int tr = it * kRowsPerInst + lane / Q;
-        const int q = lane % Q;
-        v4u v = *reinterpret_cast<const v4u*>(region + tr * kRow + ((q ^ (tr % Q)) * 16));
-        if ((tr / Q) & 1) v = (v4u){v[2], v[3], v[0], v[1]};
-        const int64_t tok = tok0 + tr;
+        const v4u v = *reinterpret_cast<const v4u*>(rbase + it * kRowsPerInst * kRowPad);
+        const int64_t tok = tok0 + it * kRowsPerInst + lane / Q;
         if (tok < M) *reinterpret_cast<v4u*>(out + tok * ld + col0 + q * 8) = v;
     }
-    __syncthreads();
+    wave_lds_fence();
 }
 
-// One K stage of the main loop on ring slot `cur` (static).  ISSUE: also
-// enqueue the loads of stage kt+2 into slot `fill`; NEXT: prefetch the scales
-// and first fragments of stage kt+1 from slot `nxt` after the barrier.
-template <bool ISSUE, bool NEXT>
-__device__ __forceinline__ void k_stage(v16f (&acc)[4][2], Frags& f0, Frags& f1, uint32_t* wsc, uint32_t* xsc,
-                                        uint8_t* cur, uint8_t* nxt, uint8_t* fill, const GemmArgs& g,
-                                        const LoadPlan& plan, int kt, int wave, int lane, int wn, int wm, int r32,
-                                        int h) {
-    uint32_t wsn[4], xsn[2];
-    if (ISSUE) issue_stage(fill, g, plan, kt + 2, wave, lane);
+// One K stage of the main loop on ring slot `cur`.  ISSUE: also enqueue the
+// loads of stage kt + kRing - 1 into slot `fill`; NEXT: after the barrier
+// (which waits until at most VM of this wave's loads are in flight, i.e.
+// stage kt+1 landed), prefetch the scales and first fragments of stage kt+1
+// from slot `nxt`.
+template <bool ISSUE, bool NEXT, int VM>
+__device__ __forceinline__ void k_stage(v16f (&acc)[4][4], Frags& f0, Frags& f1, uint32_t* wsc, uint32_t* xsc,
+                                        uint8_t* cur, uint8_t* nxt, uint8_t* fill, const Operands& ops,
+                                        const LoadPlan& plan, int kt, int wave, int wn, int wm, int r32, int h) {
+    uint32_t wsn[4], xsn[4];
+    if (ISSUE) issue_stage(fill, ops, plan, kt + kRing - 1, wave);
     read_frags(f1, cur, wn, wm, r32, h, 1);
     mfma_step<0>(acc, f0, wsc, xsc);
-    if (ISSUE) sched_step0(); else sched_step1();
+    sched_step0<ISSUE>();
     if (NEXT) {
-        // Stage kt+1 landed (only stage kt+2's loads may remain) and this
-        // stage's fragments are in registers: after the barrier stage kt+1
-        // may be read and stage kt overwritten.
-        ring_barrier<ISSUE ? kDmaPerStage : 0>();
+        // This stage's fragments are in registers and stage kt+1 landed:
+        // after the barrier stage kt+1 may be read and stage kt overwritten.
+        ring_barrier<VM>();
         read_scales(wsn, xsn, nxt, wn, wm, r32, h);
         read_frags(f0, nxt, wn, wm, r32, h, 0);
     }
@@ -314,88 +384,37 @@ __device__ __forceinline__ void k_stage(v16f (&acc)[4][2], Frags& f0, Frags& f1,
     if (NEXT) {
         sched_step1();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wsc[i] = wsn[i];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) xsc[i] = xsn[i];
+        for (int i = 0; i < 4; ++i) {
+            wsc[i] = wsn[i];
+            xsc[i] = xsn[i];
+        }
     }
 }
 
-template <int EPI, bool OUT_BF16, int REM>
-__global__ __launch_bounds__(256, 2) void gemm_fp4_kernel(GemmArgs g) {
-    __shared__ __attribute__((aligned(1024))) uint8_t ring0[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t ring1[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t ring2[kStageBytes];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wn = wave & 1;              // channel half of the workgroup tile (128 channels)
-    const int wm = wave >> 1;             // token half (64 tokens)
-    const int64_t tiles_n = g.N / kBN;
-    const int64_t tiles_m = (g.M + kBM - 1) / kBM;
-    int64_t tm, tn;
-    tile_of(blockIdx.x, (int64_t)gridDim.x, tiles_n, tiles_m, tm, tn);
-    const int64_t n0 = tn * kBN;
-    const int64_t m0 = tm * kBM;
-    const int kt_count = (int)(g.K / kBK);   // even and >= 2 (K % 256 == 0)
-
-    v16f acc[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = (v16f){};
-
-    const int r32 = lane & 31;
-    const int h = lane >> 5;
-
-    // Ring slot of stage j is (j + OFF) % 3 with OFF chosen so that the
-    // REM = (kt_count - 2) % 3 stages before the unrolled loop absorb the
-    // remainder: the loop then always starts on slot 0 and the last two
-    // stages always sit in slots 0 and 1, all known at compile time.
-    constexpr int OFF = (3 - REM) % 3;
-    uint8_t* const slots[3] = {ring0, ring1, ring2};
-    const LoadPlan plan = make_plan(g, n0, m0, wave, lane);
-    issue_stage(slots[OFF % 3], g, plan, 0, wave, lane);
-    issue_stage(slots[(OFF + 1) % 3], g, plan, 1, wave, lane);
-    ring_barrier<kDmaPerStage>();                    // stage 0 landed
-
-    Frags f0, f1;
-    uint32_t wsc[4], xsc[2];
-    read_scales(wsc, xsc, slots[OFF % 3], wn, wm, r32, h);
-    read_frags(f0, slots[OFF % 3], wn, wm, r32, h, 0);
-
-#define FP4DIT_STAGE(ISSUE, NEXT, CUR, NXT, FILL, KT) \
-    k_stage<ISSUE, NEXT>(acc, f0, f1, wsc, xsc, slots[CUR], slots[NXT], slots[FILL], g, plan, KT, wave, lane, \
-                         wn, wm, r32, h)
-    // stages 0 .. REM-1 (each issues the loads of stage j + 2)
-    if (REM >= 1) FP4DIT_STAGE(true, true, (OFF + 0) % 3, (OFF + 1) % 3, (OFF + 2) % 3, 0);
-    if (REM >= 2) FP4DIT_STAGE(true, true, (OFF + 1) % 3, (OFF + 2) % 3, (OFF + 0) % 3, 1);
-    // stages REM .. kt_count - 3, three at a time, on slots 0, 1, 2
-    for (int kt = REM; kt < kt_count - 2; kt += 3) {
-        FP4DIT_STAGE(true, true, 0, 1, 2, kt);
-        FP4DIT_STAGE(true, true, 1, 2, 0, kt + 1);
-        FP4DIT_STAGE(true, true, 2, 0, 1, kt + 2);
-    }
-    // the last two stages: no more loads
-    FP4DIT_STAGE(false, true, 0, 1, 2, kt_count - 2);
-    FP4DIT_STAGE(false, false, 1, 2, 0, kt_count - 1);
-#undef FP4DIT_STAGE
-    __syncthreads();                      // the epilogue reuses the LDS ring
-
-    // ------------------------------------------------------------ epilogue --
-    // acc[nb][mb][i]: channel n0 + wn*128 + nb*32 + 8*(i/4) + 4h + i%4,
-    //                 token   m0 + wm*64 + mb*32 + r32.
+// Epilogue of one tile: per-head RMSNorm / SwiGLU (+ MXFP4 requant) / plain
+// cast on the accumulators, then the single store.  `stg` is the LDS ring
+// slot left free by the next tile's prefetch: each wave stages its bf16
+// rows in its own 8 KiB region of it, and the per-token head sums of a
+// 256-wide head (both channel halves) are exchanged through its last 2 KiB.
+// acc[nb][mb][i]: channel n0 + wn*128 + nb*32 + 8*(i/4) + 4h + i%4,
+//                 token   m0 + wm*128 + mb*32 + r32.
+template <int EPI, bool OUT_BF16>
+__device__ __forceinline__ void epilogue(v16f (&acc)[4][4], const GemmArgs& g, int64_t n0, int64_t m0,
+                                         uint8_t* stg, int wave, int lane_) {
+    const int lane = (int)opaque_vgpr((uint32_t)lane_);
+    const int wn = wave & 1, wm = wave >> 1;
+    const int r32 = lane & 31, h = lane >> 5;
     const int64_t cbase = n0 + wn * 128;
-    const int64_t tok0 = m0 + wm * 64;
-    uint8_t* region = wave == 0 ? ring0 : wave == 1 ? ring1 : wave == 2 ? ring2 : ring0 + kStageOutBytes;
+    const int64_t tok0 = m0 + wm * 128;
+    uint8_t* region = stg + wave * kStageOutBytes;
     if (EPI == kEpiNone || EPI == kEpiRmsNorm) {
-        float rstd[2] = {1.f, 1.f};
+        float rstd[4] = {1.f, 1.f, 1.f, 1.f};
         bool norm = false;
         if (EPI == kEpiRmsNorm) {
-            float* red = reinterpret_cast<float*>(ring1 + kRedOff);  // [2 wn][128 tokens]
-            float ss[2];
+            float* red = reinterpret_cast<float*>(stg + kRedOff);   // [2 wn][256 tokens]
+            float ss[4];
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
+            for (int mb = 0; mb < 4; ++mb) {
                 float s = 0.f;
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb)
@@ -406,17 +425,18 @@ __global__ __launch_bounds__(256, 2) void gemm_fp4_kernel(GemmArgs g) {
             if (g.head_dim == 256) {                      // head = both channel halves
                 if (h == 0) {
 #pragma unroll
-                    for (int mb = 0; mb < 2; ++mb) red[wn * kBM + wm * 64 + mb * 32 + r32] = ss[mb];
+                    for (int mb = 0; mb < 4; ++mb) red[wn * kBM + wm * 128 + mb * 32 + r32] = ss[mb];
                 }
-                __syncthreads();
+                ring_barrier<63>();                       // LDS only: the prefetch stays in flight
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb) ss[mb] += red[(1 - wn) * kBM + wm * 64 + mb * 32 + r32];
+                for (int mb = 0; mb < 4; ++mb) ss[mb] += red[(1 - wn) * kBM + wm * 128 + mb * 32 + r32];
+                ring_barrier<63>();                       // red overlaps the rows staged next
             }
             const int64_t head0 = g.head_dim == 256 ? n0 : cbase;
             norm = head0 < g.n_norm;
             const float inv_d = 1.0f / (float)g.head_dim;
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) rstd[mb] = rsqrtf(ss[mb] * inv_d + g.eps);
+            for (int mb = 0; mb < 4; ++mb) rstd[mb] = rsqrtf(ss[mb] * inv_d + g.eps);
         }
         v4f wv[4][4];
 #pragma unroll
@@ -434,22 +454,21 @@ __global__ __launch_bounds__(256, 2) void gemm_fp4_kernel(GemmArgs g) {
                 v[r] = (EPI == kEpiRmsNorm && norm) ? acc[nb][mb][4 * a + r] * rstd[mb] * wv[nb][a][r]
                                                     : acc[nb][mb][4 * a + r];
         };
-        if (OUT_BF16) {
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 4; ++mb) {
+            if (OUT_BF16) {
                 store_bf16_half<16>(region, [&](int q, float* v) { vals(q, mb, v); }, static_cast<uint16_t*>(g.out),
                                     g.N, tok0 + mb * 32, cbase, g.M, r32, h, lane);
-        } else {
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
+            } else {
                 const int64_t tok = tok0 + mb * 32 + r32;
-                if (tok >= g.M) continue;
+                if (tok < g.M) {
 #pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    float v[4];
-                    vals(q, mb, v);
-                    *reinterpret_cast<v4f*>(static_cast<float*>(g.out) + tok * g.N + cbase + (q >> 2) * 32 +
-                                            8 * (q & 3) + 4 * h) = (v4f){v[0], v[1], v[2], v[3]};
+                    for (int q = 0; q < 16; ++q) {
+                        float v[4];
+                        vals(q, mb, v);
+                        *reinterpret_cast<v4f*>(static_cast<float*>(g.out) + tok * g.N + cbase + (q >> 2) * 32 +
+                                                8 * (q & 3) + 4 * h) = (v4f){v[0], v[1], v[2], v[3]};
+                    }
                 }
             }
         }
@@ -461,53 +480,44 @@ __global__ __launch_bounds__(256, 2) void gemm_fp4_kernel(GemmArgs g) {
         // outputs cbase/2 + 32p + 8a + 4h + r.
         const int64_t nh = g.N / 2;
         const int64_t ob0 = cbase / 2;
-        float hv[2][2][16];                   // [p][mb][4a + r]
 #pragma unroll
-        for (int p = 0; p < 2; ++p)
+        for (int mb = 0; mb < 4; ++mb) {
+            float hv[2][16];                  // [p][4a + r]
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+            for (int p = 0; p < 2; ++p)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) hv[p][mb][i] = silu_f(acc[2 * p][mb][i]) * acc[2 * p + 1][mb][i];
-        if (g.out != nullptr) {
-            if (OUT_BF16) {
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
+                for (int i = 0; i < 16; ++i) hv[p][i] = silu_f(acc[2 * p][mb][i]) * acc[2 * p + 1][mb][i];
+            const int64_t tok = tok0 + mb * 32 + r32;
+            if (g.out != nullptr) {
+                if (OUT_BF16) {
                     store_bf16_half<8>(region, [&](int q, float* v) {
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) v[r] = hv[q >> 2][mb][4 * (q & 3) + r];
+                        for (int r = 0; r < 4; ++r) v[r] = hv[q >> 2][4 * (q & 3) + r];
                     }, static_cast<uint16_t*>(g.out), nh, tok0 + mb * 32, ob0, g.M, r32, h, lane);
-            } else {
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb) {
-                    const int64_t tok = tok0 + mb * 32 + r32;
-                    if (tok >= g.M) continue;
+                } else if (tok < g.M) {
 #pragma unroll
                     for (int p = 0; p < 2; ++p)
 #pragma unroll
                         for (int a = 0; a < 4; ++a)
                             *reinterpret_cast<v4f*>(static_cast<float*>(g.out) + tok * nh + ob0 + 32 * p + 8 * a +
                                                     4 * h) =
-                                (v4f){hv[p][mb][4 * a], hv[p][mb][4 * a + 1], hv[p][mb][4 * a + 2], hv[p][mb][4 * a + 3]};
+                                (v4f){hv[p][4 * a], hv[p][4 * a + 1], hv[p][4 * a + 2], hv[p][4 * a + 3]};
                 }
             }
-        }
-        if (g.out_codes != nullptr) {
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                const int64_t tok = tok0 + mb * 32 + r32;
+            if (g.out_codes != nullptr) {
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
                     uint32_t amax = 0u;
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const uint32_t a = __float_as_uint(hv[p][mb][i]) & 0x7FFFFFFFu;
+                        const uint32_t a = __float_as_uint(hv[p][i]) & 0x7FFFFFFFu;
                         amax = a > amax ? a : amax;
                     }
                     amax = max_xor32_u(amax);
                     const uint32_t sc = e8m0_from_amax_bits(amax);
                     uint32_t c16[4];                  // codes of outputs 8a+4h .. +3
 #pragma unroll
-                    for (int a = 0; a < 4; ++a) c16[a] = sc == 0xFFu ? 0u : e2m1_pack4(&hv[p][mb][4 * a], sc);
+                    for (int a = 0; a < 4; ++a) c16[a] = sc == 0xFFu ? 0u : e2m1_pack4(&hv[p][4 * a], sc);
                     // lane h=0 stores bytes 0..7 of the block (outputs 0..15),
                     // lane h=1 bytes 8..15; each needs two halves from its partner.
                     const uint32_t send = h == 0 ? (c16[2] | (c16[3] << 16)) : (c16[0] | (c16[1] << 16));
@@ -531,27 +541,157 @@ __global__ __launch_bounds__(256, 2) void gemm_fp4_kernel(GemmArgs g) {
     }
 }
 
+// Persistent kernel: workgroup b runs tiles b, b + G, b + 2G, ... (G = grid
+// size, a multiple of 8 so every tile of one workgroup maps to its own XCD).
+// While a tile's epilogue runs, the first NS - 1 K stages of the next tile
+// are already loading into the other ring slots.
+// NS: ring depth of this instance (kRing, or fewer for short K); PEEL:
+// (K/128 - NS + 1) % NS, the stages run before the unrolled loop.
+template <int EPI, bool OUT_BF16, int NS, int PEEL>
+__global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
+    static_assert(NS >= 2 && NS <= kRing && PEEL < NS, "ring shape");
+    __shared__ __attribute__((aligned(1024))) uint8_t ring0[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring1[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring2[NS > 2 ? kStageBytes : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring3[NS > 3 ? kStageBytes : 16];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wn = wave & 1;              // channel half of the workgroup tile (128 channels)
+    const int wm = wave >> 1;             // token half (128 tokens)
+    const int r32 = lane & 31;
+    const int h = lane >> 5;
+    const int M = (int)g.M, K = (int)g.K;    // M * K / 2 < 2^31 (checked by the host)
+    const int tiles_n = (int)(g.N / kBN);
+    const int tiles_m = (M + kBM - 1) / kBM;
+    const int n_tiles = tiles_n * tiles_m;
+    const int kt_count = K / kBK;            // even, >= NS - 1 (chosen by the host)
+    const Operands ops = make_operands(g);
+
+    // Stage j lives in ring slot (j + OFF) % NS.  The first PEEL stages run
+    // before the unrolled loop, so the loop always starts on slot 0 and the
+    // last NS - 1 stages sit in slots 0 .. NS - 2: every slot index is a
+    // compile-time constant, and slot OFF - 1 (mod NS) is the one the next
+    // tile's prefetch leaves free for the epilogue.
+    constexpr int D = NS - 1;                          // prefetch distance (stages)
+    constexpr int OFF = (NS - PEEL) % NS;
+    constexpr int kVmSteady = (D - 1) * kDmaPerStage;  // loads allowed in flight at a barrier
+    uint8_t* const slots[4] = {ring0, ring1, ring2, ring3};
+    uint8_t* const stg = slots[(OFF + D) % NS];
+    const int n_issue = kt_count - D;
+
+    int v = blockIdx.x;
+    int tm, tn;
+    tile_of(v, n_tiles, tiles_n, tiles_m, tm, tn);
+    LoadPlan plan = make_plan(M, K, tn * kBN, tm * kBM, wave, lane);
+    static_for<0, D>([&](auto j) { issue_stage(slots[(j() + OFF) % NS], ops, plan, j(), wave); });
+
+    for (;;) {
+        const int n0 = tn * kBN;
+        const int m0 = tm * kBM;
+        v16f acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = (v16f){};
+
+        ring_barrier<kVmSteady>();                     // stage 0 landed
+        Frags f0, f1;
+        uint32_t wsc[4], xsc[4];
+        read_scales(wsc, xsc, slots[OFF % NS], wn, wm, r32, h);
+        read_frags(f0, slots[OFF % NS], wn, wm, r32, h, 0);
+
+        // stages 0 .. PEEL-1 (each issues the loads of stage j + D)
+        static_for<0, PEEL>([&](auto j) {
+            k_stage<true, true, kVmSteady>(acc, f0, f1, wsc, xsc, slots[(j() + OFF) % NS],
+                                           slots[(j() + OFF + 1) % NS], slots[(j() + OFF + D) % NS], ops, plan, j(),
+                                           wave, wn, wm, r32, h);
+        });
+        // stages PEEL .. kt_count - NS, NS at a time, on slots 0 .. NS-1
+        for (int kt = PEEL; kt < n_issue; kt += NS) {
+            static_for<0, NS>([&](auto s) {
+                k_stage<true, true, kVmSteady>(acc, f0, f1, wsc, xsc, slots[s()], slots[(s() + 1) % NS],
+                                               slots[(s() + D) % NS], ops, plan, kt + s(), wave, wn, wm, r32, h);
+            });
+        }
+        // the last D stages: no more loads; stage n_issue + i waits for the
+        // D - 2 - i stages still behind the next one
+        static_for<0, D>([&](auto i) {
+            constexpr int kI = decltype(i)::value;
+            constexpr int kVm = kI < D - 1 ? (D - 2 - kI) * kDmaPerStage : 0;
+            k_stage<false, (kI < D - 1), kVm>(acc, f0, f1, wsc, xsc, slots[kI], slots[(kI + 1) % NS], slots[0], ops,
+                                              plan, n_issue + kI, wave, wn, wm, r32, h);
+        });
+        ring_barrier<63>();                            // every wave is done reading the ring
+
+        const int vn = v + (int)gridDim.x;
+        const bool more = vn < n_tiles;
+        if (more) {                                    // prefetch the next tile, then finish this one
+            tile_of(vn, n_tiles, tiles_n, tiles_m, tm, tn);
+            plan = make_plan(M, K, tn * kBN, tm * kBM, wave, lane);
+            static_for<0, D>([&](auto j) { issue_stage(slots[(j() + OFF) % NS], ops, plan, j(), wave); });
+        }
+        epilogue<EPI, OUT_BF16>(acc, g, n0, m0, stg, wave, lane);
+        if (!more) break;
+        v = vn;
+    }
+}
+
+// K/128 is even, so with a 4-deep ring PEEL = (K/128 - 3) % 4 is 1 or 3, and
+// the 3-deep ring only serves K/128 = 2 (PEEL 0): only those are built.
+template <int EPI, bool OUT_BF16, int NS>
+void launch_peel(const GemmArgs& g, int peel, dim3 grid, hipStream_t stream) {
+    static_for<0, NS>([&](auto p) {
+        constexpr int kPeel = decltype(p)::value;
+        constexpr bool kBuilt = NS == 4 ? (kPeel % 2 == 1) : kPeel == 0;
+        if constexpr (kBuilt) {
+            if (peel == kPeel)
+                hipLaunchKernelGGL((gemm_fp4_kernel<EPI, OUT_BF16, NS, kPeel>), grid, dim3(256), 0, stream, g);
+        }
+    });
+}
+
+// Ring depth kRing needs at least kRing - 1 K stages; shorter K (K = 256:
+// two stages) runs a 3-deep ring.
 template <int EPI, bool OUT_BF16>
-void launch_rem(const GemmArgs& g, dim3 grid, hipStream_t stream) {
-    switch ((g.K / kBK - 2) % 3) {
-        case 0: hipLaunchKernelGGL((gemm_fp4_kernel<EPI, OUT_BF16, 0>), grid, dim3(256), 0, stream, g); break;
-        case 1: hipLaunchKernelGGL((gemm_fp4_kernel<EPI, OUT_BF16, 1>), grid, dim3(256), 0, stream, g); break;
-        default: hipLaunchKernelGGL((gemm_fp4_kernel<EPI, OUT_BF16, 2>), grid, dim3(256), 0, stream, g); break;
+void launch_ring(const GemmArgs& g, dim3 grid, hipStream_t stream) {
+    const int kt_count = (int)(g.K / kBK);
+    if (kt_count >= kRing - 1) {
+        launch_peel<EPI, OUT_BF16, kRing>(g, (kt_count - (kRing - 1)) % kRing, grid, stream);
+    } else {
+        launch_peel<EPI, OUT_BF16, 3>(g, (kt_count - 2) % 3, grid, stream);
     }
 }
 
 template <int EPI>
 void launch_epi(const GemmArgs& g, bool out_bf16, dim3 grid, hipStream_t stream) {
     if (out_bf16) {
-        launch_rem<EPI, true>(g, grid, stream);
+        launch_ring<EPI, true>(g, grid, stream);
     } else {
-        launch_rem<EPI, false>(g, grid, stream);
+        launch_ring<EPI, false>(g, grid, stream);
     }
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 hipError_t launch_gemm(const GemmArgs& g, int epi, bool out_bf16, hipStream_t stream) {
     const int64_t tiles = (g.N / kBN) * ((g.M + kBM - 1) / kBM);
-    const dim3 grid((unsigned)tiles);
+    // one workgroup per CU, a multiple of 8 (the XCD count) when persistent
+    const int64_t cus = device_cus();
+    const int64_t wgs = tiles <= cus ? tiles : (cus >= 8 ? cus & ~int64_t(7) : cus);
+    const dim3 grid((unsigned)wgs);
     switch (epi) {
         case kEpiNone: launch_epi<kEpiNone>(g, out_bf16, grid, stream); break;
         case kEpiRmsNorm: launch_epi<kEpiRmsNorm>(g, out_bf16, grid, stream); break;
