@@ -277,10 +277,9 @@ def main():
     Ld, Lq = layers[dom], layers[quant_dom]
     achieved = Ld.flops / (g_avg * 1e-3) / 1e12
     # kernel instantiation as rocprof names it: epilogue, bf16 output, LDS ring
-    # depth (4, or 3 when K = 256) and the K stages peeled before its loop
+    # depth (3) and the K stages peeled before its unrolled loop
     out_bf16 = Ld.out is not None
-    kt = Ld.k // 128
-    ring = 4 if kt >= 3 else 3
+    kt, ring = Ld.k // 128, 3
     kernel_key = "gemm_%s<%s,%d,%d>" % (Ld.wl.epilogue, "true" if out_bf16 else "false", ring, (kt - ring + 1) % ring)
 
     out = {

@@ -50,7 +50,7 @@ namespace {
 constexpr int kBN = 256;               // channels per workgroup
 constexpr int kBM = 256;               // tokens per workgroup
 constexpr int kBK = 128;               // K elements per LDS stage
-constexpr int kRing = 4;               // LDS ring depth (stages)
+constexpr int kRing = 3;               // LDS ring depth (stages)
 constexpr int kRowBytes = kBK / 2;     // 64 bytes of codes per row per stage
 constexpr int kScaleBytes = kBK / 32;  // 4 scale bytes per row per stage
 constexpr int kWCodesOff = 0;
@@ -89,12 +89,20 @@ struct GemmArgs {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Compile-time loop: f(integral_constant<int, I>) for I = B .. E-1.
+// Compile-time loop: f(integral_constant<int, I>) for I = B .. E-1 (device
+// code; static_for_host for the launchers).
 template <int B, int E, typename F>
-__host__ __device__ __forceinline__ void static_for(F&& f) {
+__device__ __forceinline__ void static_for(F&& f) {
     if constexpr (B < E) {
         f(std::integral_constant<int, B>());
         static_for<B + 1, E>(f);
+    }
+}
+template <int B, int E, typename F>
+void static_for_host(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>());
+        static_for_host<B + 1, E>(f);
     }
 }
 
@@ -202,14 +210,12 @@ __device__ __forceinline__ Operands make_operands(const GemmArgs& g) {
     return o;
 }
 
-// Enqueue the 10 direct-to-LDS loads of K stage kt into `stage` (this wave's
-// share; `wave` is wave-uniform).
-__device__ __forceinline__ void issue_stage(uint8_t* stage, const Operands& o, const LoadPlan& p, int kt,
-                                            int wave) {
+// Enqueue the 10 direct-to-LDS loads of K stage kt (this wave's share).
+// codes / scales: LDS byte addresses of this wave's part of the stage's code
+// and scale areas (stage + wave * 4096, stage + wave * 256).
+__device__ __forceinline__ void issue_stage(uint32_t codes, uint32_t scales, const Operands& o, const LoadPlan& p,
+                                            int kt) {
     const uint32_t soff = (uint32_t)kt * 128u;
-    const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(stage);
-    const uint32_t codes = opaque_sgpr(lds0 + wave * 4096);       // this wave's 4 x 1 KiB of W and of X
-    const uint32_t scales = opaque_sgpr(lds0 + wave * 256);       // its 256 B of W and of X scales
     auto lds = [](uint32_t a) { return (lds_void*)(uintptr_t)a; };
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -220,16 +226,47 @@ __device__ __forceinline__ void issue_stage(uint8_t* stage, const Operands& o, c
     __builtin_amdgcn_raw_ptr_buffer_load_lds(o.xs, lds(scales + kXScalesOff), 4, p.x_scale, soff, 0, 0);
 }
 
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) { return (uint32_t)reinterpret_cast<uintptr_t>(p); }
+
+// Load l (0..9) of a stage: 0..3 weight codes, 4..7 token codes, 8 weight
+// scales, 9 token scales (the same loads as issue_stage, one at a time; l is
+// a compile-time constant at every call, so the switch folds away).
+__device__ __forceinline__ void issue_load(int l, uint32_t codes, uint32_t scales, const Operands& o,
+                                           const LoadPlan& p, uint32_t soff) {
+    auto lds = [](uint32_t a) { return (lds_void*)(uintptr_t)a; };
+    switch (l) {
+        case 0: case 1: case 2: case 3:
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(o.wc, lds(codes + kWCodesOff + l * 1024), 16, p.w_code[l], soff, 0,
+                                                     0);
+            break;
+        case 4: case 5: case 6: case 7:
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(o.xc, lds(codes + kXCodesOff + (l - 4) * 1024), 16, p.x_code[l - 4],
+                                                     soff, 0, 0);
+            break;
+        case 8:
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(o.ws, lds(scales + kWScalesOff), 4, p.w_scale, soff, 0, 0);
+            break;
+        default:
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(o.xs, lds(scales + kXScalesOff), 4, p.x_scale, soff, 0, 0);
+            break;
+    }
+}
+
+// Whole-stage prefetch outside the K loop (prologue of a tile).
+__device__ __forceinline__ void issue_stage_at(uint8_t* stage, const Operands& o, const LoadPlan& p, int kt,
+                                               int wave) {
+    const uint32_t codes = opaque_sgpr(lds_addr(stage) + wave * 4096);
+    const uint32_t scales = opaque_sgpr(lds_addr(stage) + wave * 256);
+    issue_stage(codes, scales, o, p, kt);
+}
+
 struct Frags {
     v4i w[4], x[4];
 };
 
 // Fragment reads of K-step s: lane group h takes MX block 2h + s of the stage.
-// The slot pointer gets an opaque zero offset so that its per-lane addresses
-// are formed at each use (one add) rather than kept live for every slot.
-__device__ __forceinline__ void read_frags(Frags& f, const uint8_t* stage_, int wn, int wm, int r32, int h,
+__device__ __forceinline__ void read_frags(Frags& f, const uint8_t* stage, int wn, int wm, int r32, int h,
                                            int s) {
-    const uint8_t* stage = stage_ + opaque_sgpr(0u);
     const int chunk = ((2 * h + s) ^ ((r32 >> 2) & 3)) * 16;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -239,69 +276,18 @@ __device__ __forceinline__ void read_frags(Frags& f, const uint8_t* stage_, int 
         f.x[i] = *reinterpret_cast<const v4i*>(stage + kXCodesOff + (wm * 128 + i * 32 + r32) * kRowBytes + chunk);
 }
 
-// Scale bytes 2h, 2h+1 of every fragment row (byte s serves K-step s),
-// read as the row's whole dword: a 16-bit LDS read here makes the compiler
-// wait for every load still in flight (it cannot tell it apart from the
-// loads landing in the other ring slots), a 32-bit one does not.
-__device__ __forceinline__ void read_scales(uint32_t* wsc, uint32_t* xsc, const uint8_t* stage_, int wn, int wm,
+// Scale bytes 2h, 2h+1 of every fragment row (byte s serves K-step s, picked
+// by op_sel), read as one 16-bit value so that no per-lane shift is needed.
+__device__ __forceinline__ void read_scales(uint32_t* wsc, uint32_t* xsc, const uint8_t* stage, int wn, int wm,
                                             int r32, int h) {
-    const uint8_t* stage = stage_ + opaque_sgpr(0u);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        wsc[i] = *reinterpret_cast<const uint32_t*>(stage + kWScalesOff + (wn * 128 + i * 32 + r32) * kScaleBytes) >> (16 * h);
+        wsc[i] = *reinterpret_cast<const uint16_t*>(stage + kWScalesOff + (wn * 128 + i * 32 + r32) * kScaleBytes + 2 * h);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        xsc[i] = *reinterpret_cast<const uint32_t*>(stage + kXScalesOff + (wm * 128 + i * 32 + r32) * kScaleBytes) >> (16 * h);
+        xsc[i] = *reinterpret_cast<const uint16_t*>(stage + kXScalesOff + (wm * 128 + i * 32 + r32) * kScaleBytes + 2 * h);
 }
 
-template <int S>
-__device__ __forceinline__ void mfma_step(v16f (&acc)[4][4], const Frags& f, const uint32_t* wsc,
-                                          const uint32_t* xsc) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const v8i a = {f.w[i][0], f.w[i][1], f.w[i][2], f.w[i][3], 0, 0, 0, 0};
-            const v8i b = {f.x[j][0], f.x[j][1], f.x[j][2], f.x[j][3], 0, 0, 0, 0};
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 4, 4, S, (int)wsc[i],
-                                                                        S, (int)xsc[j]);
-        }
-}
-
-// Scheduling of one K-step's 16 MFMAs (masks: 0x008 MFMA, 0x020 VMEM read,
-// 0x100 DS read).  First K-step of a stage: interleaved with the 8 fragment
-// reads of the second and, when loads are issued, the 10 direct-to-LDS loads
-// of a later stage.  Second K-step (after the barrier): interleaved with the
-// 8 scale and 8 fragment reads of the next stage.
-template <bool ISSUE>
-__device__ __forceinline__ void sched_step0() {
-    static_for<0, 8>([&](auto) {
-        if (ISSUE) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    });
-    if (ISSUE) {
-        static_for<0, 2>([&](auto) {
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        });
-        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
-    } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-}
-__device__ __forceinline__ void sched_step1() {
-    static_for<0, 16>([&](auto) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    });
-    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // the 8 scale shifts, once the reads landed
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-// silu(z) = z * sigmoid(z), with the hardware exp2 and reciprocal (about
-// 1 ulp each): far inside the fp32 tolerance of the epilogue.
 __device__ __forceinline__ float silu_f(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Map the linear workgroup id to a (token tile, channel tile).  Workgroups
@@ -359,30 +345,81 @@ __device__ __forceinline__ void store_bf16_half(uint8_t* region, F vals, uint16_
     wave_lds_fence();
 }
 
-// One K stage of the main loop on ring slot `cur`.  ISSUE: also enqueue the
-// loads of stage kt + kRing - 1 into slot `fill`; NEXT: after the barrier
-// (which waits until at most VM of this wave's loads are in flight, i.e.
-// stage kt+1 landed), prefetch the scales and first fragments of stage kt+1
-// from slot `nxt`.
+// One MFMA of K-step S: accumulator block (i, j) = weight fragment i x token
+// fragment j.
+template <int S>
+__device__ __forceinline__ void mfma_one(v16f& acc, const v4i& w, const v4i& x, uint32_t ws, uint32_t xs) {
+    const v8i a = {w[0], w[1], w[2], w[3], 0, 0, 0, 0};
+    const v8i b = {x[0], x[1], x[2], x[3], 0, 0, 0, 0};
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 4, 4, S, (int)ws, S, (int)xs);
+}
+
+// Fragment r (0..3 weight rows i = r, 4..7 token rows j = r - 4) of K-step s.
+template <int R>
+__device__ __forceinline__ void read_frag(Frags& f, const uint8_t* stage, int wn, int wm, int r32, int h, int s) {
+    const int chunk = ((2 * h + s) ^ ((r32 >> 2) & 3)) * 16;
+    if constexpr (R < 4)
+        f.w[R] = *reinterpret_cast<const v4i*>(stage + kWCodesOff + (wn * 128 + R * 32 + r32) * kRowBytes + chunk);
+    else
+        f.x[R - 4] = *reinterpret_cast<const v4i*>(stage + kXCodesOff + (wm * 128 + (R - 4) * 32 + r32) * kRowBytes +
+                                                   chunk);
+}
+
+// Scale pair r (0..3 weight rows, 4..7 token rows) of a stage: bytes 2h, 2h+1
+// of the row (byte s serves K-step s, picked by op_sel), one 16-bit read.
+template <int R>
+__device__ __forceinline__ void read_scale(uint32_t* wsc, uint32_t* xsc, const uint8_t* stage, int wn, int wm, int r32,
+                                           int h) {
+    if constexpr (R < 4)
+        wsc[R] = *reinterpret_cast<const uint16_t*>(stage + kWScalesOff + (wn * 128 + R * 32 + r32) * kScaleBytes + 2 * h);
+    else
+        xsc[R - 4] = *reinterpret_cast<const uint16_t*>(stage + kXScalesOff + (wm * 128 + (R - 4) * 32 + r32) * kScaleBytes +
+                                                        2 * h);
+}
+
+// One K stage of the main loop on ring slot `cur`, scheduled by hand (each
+// sched_barrier pins the instructions issued since the previous one):
+// * K-step 0: MFMA n on the fragments read one step earlier, with load n of
+//   stage kt + kRing - 1 (n < 10, ISSUE) and the read of second-step
+//   fragment n (n < 8);
+// * barrier (NEXT): this wave's stage-kt+1 loads landed (at most VM loads
+//   remain in flight) and every wave is done with stage kt;
+// * K-step 1: the 8 scale and 8 fragment reads of stage kt+1 go out with the
+//   first 8 MFMAs, so that they have landed long before K-step 0 of the next
+//   stage needs them.
 template <bool ISSUE, bool NEXT, int VM>
 __device__ __forceinline__ void k_stage(v16f (&acc)[4][4], Frags& f0, Frags& f1, uint32_t* wsc, uint32_t* xsc,
-                                        uint8_t* cur, uint8_t* nxt, uint8_t* fill, const Operands& ops,
+                                        uint8_t* cur_, uint8_t* nxt_, uint8_t* fill, const Operands& ops,
                                         const LoadPlan& plan, int kt, int wave, int wn, int wm, int r32, int h) {
+    // The stage's LDS bases, made opaque in one statement ahead of all its
+    // memory operations: the compiler then forms each address at its use
+    // (one add) instead of keeping one live register per ring slot and load.
+    uint32_t fill_codes = lds_addr(fill) + wave * 4096, fill_scales = lds_addr(fill) + wave * 256, zero = 0;
+    asm volatile("" : "+s"(fill_codes), "+s"(fill_scales), "+s"(zero));
+    const uint8_t* cur = cur_ + zero;
+    const uint8_t* nxt = nxt_ + zero;
+    const uint32_t soff = (uint32_t)(kt + kRing - 1) * 128u;
+    static_for<0, 16>([&](auto n) {
+        constexpr int kN = decltype(n)::value;
+        mfma_one<0>(acc[kN / 4][kN % 4], f0.w[kN / 4], f0.x[kN % 4], wsc[kN / 4], xsc[kN % 4]);
+        if constexpr (ISSUE && kN < 10) issue_load(kN, fill_codes, fill_scales, ops, plan, soff);
+        if constexpr (kN < 8) read_frag<kN>(f1, cur, wn, wm, r32, h, 1);
+        __builtin_amdgcn_sched_barrier(0);
+    });
     uint32_t wsn[4], xsn[4];
-    if (ISSUE) issue_stage(fill, ops, plan, kt + kRing - 1, wave);
-    read_frags(f1, cur, wn, wm, r32, h, 1);
-    mfma_step<0>(acc, f0, wsc, xsc);
-    sched_step0<ISSUE>();
+    if (NEXT) ring_barrier<VM>();
+    static_for<0, 16>([&](auto n) {
+        constexpr int kN = decltype(n)::value;
+        mfma_one<1>(acc[kN / 4][kN % 4], f1.w[kN / 4], f1.x[kN % 4], wsc[kN / 4], xsc[kN % 4]);
+        if constexpr (kN < 8) {
+            if (NEXT) {
+                read_scale<kN>(wsn, xsn, nxt, wn, wm, r32, h);
+                read_frag<kN>(f0, nxt, wn, wm, r32, h, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    });
     if (NEXT) {
-        // This stage's fragments are in registers and stage kt+1 landed:
-        // after the barrier stage kt+1 may be read and stage kt overwritten.
-        ring_barrier<VM>();
-        read_scales(wsn, xsn, nxt, wn, wm, r32, h);
-        read_frags(f0, nxt, wn, wm, r32, h, 0);
-    }
-    mfma_step<1>(acc, f1, wsc, xsc);
-    if (NEXT) {
-        sched_step1();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             wsc[i] = wsn[i];
@@ -545,8 +582,8 @@ __device__ __forceinline__ void epilogue(v16f (&acc)[4][4], const GemmArgs& g, i
 // size, a multiple of 8 so every tile of one workgroup maps to its own XCD).
 // While a tile's epilogue runs, the first NS - 1 K stages of the next tile
 // are already loading into the other ring slots.
-// NS: ring depth of this instance (kRing, or fewer for short K); PEEL:
-// (K/128 - NS + 1) % NS, the stages run before the unrolled loop.
+// NS: ring depth (kRing); PEEL: (K/128 - NS + 1) % NS, the stages run before
+// the unrolled loop.
 template <int EPI, bool OUT_BF16, int NS, int PEEL>
 __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
     static_assert(NS >= 2 && NS <= kRing && PEEL < NS, "ring shape");
@@ -585,7 +622,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
     int tm, tn;
     tile_of(v, n_tiles, tiles_n, tiles_m, tm, tn);
     LoadPlan plan = make_plan(M, K, tn * kBN, tm * kBM, wave, lane);
-    static_for<0, D>([&](auto j) { issue_stage(slots[(j() + OFF) % NS], ops, plan, j(), wave); });
+    static_for<0, D>([&](auto j) { issue_stage_at(slots[(j() + OFF) % NS], ops, plan, j(), wave); });
 
     for (;;) {
         const int n0 = tn * kBN;
@@ -630,7 +667,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
         if (more) {                                    // prefetch the next tile, then finish this one
             tile_of(vn, n_tiles, tiles_n, tiles_m, tm, tn);
             plan = make_plan(M, K, tn * kBN, tm * kBM, wave, lane);
-            static_for<0, D>([&](auto j) { issue_stage(slots[(j() + OFF) % NS], ops, plan, j(), wave); });
+            static_for<0, D>([&](auto j) { issue_stage_at(slots[(j() + OFF) % NS], ops, plan, j(), wave); });
         }
         epilogue<EPI, OUT_BF16>(acc, g, n0, m0, stg, wave, lane);
         if (!more) break;
@@ -638,30 +675,21 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
     }
 }
 
-// K/128 is even, so with a 4-deep ring PEEL = (K/128 - 3) % 4 is 1 or 3, and
-// the 3-deep ring only serves K/128 = 2 (PEEL 0): only those are built.
 template <int EPI, bool OUT_BF16, int NS>
 void launch_peel(const GemmArgs& g, int peel, dim3 grid, hipStream_t stream) {
-    static_for<0, NS>([&](auto p) {
+    static_for_host<0, NS>([&](auto p) {
         constexpr int kPeel = decltype(p)::value;
-        constexpr bool kBuilt = NS == 4 ? (kPeel % 2 == 1) : kPeel == 0;
-        if constexpr (kBuilt) {
-            if (peel == kPeel)
-                hipLaunchKernelGGL((gemm_fp4_kernel<EPI, OUT_BF16, NS, kPeel>), grid, dim3(256), 0, stream, g);
-        }
+        if (peel == kPeel)
+            hipLaunchKernelGGL((gemm_fp4_kernel<EPI, OUT_BF16, NS, kPeel>), grid, dim3(256), 0, stream, g);
     });
 }
 
-// Ring depth kRing needs at least kRing - 1 K stages; shorter K (K = 256:
-// two stages) runs a 3-deep ring.
+// A kRing-deep ring needs at least kRing - 1 K stages: K >= 256 gives two.
 template <int EPI, bool OUT_BF16>
 void launch_ring(const GemmArgs& g, dim3 grid, hipStream_t stream) {
+    static_assert(kRing - 1 <= kGemmKMultiple / kBK, "ring deeper than the shortest K");
     const int kt_count = (int)(g.K / kBK);
-    if (kt_count >= kRing - 1) {
-        launch_peel<EPI, OUT_BF16, kRing>(g, (kt_count - (kRing - 1)) % kRing, grid, stream);
-    } else {
-        launch_peel<EPI, OUT_BF16, 3>(g, (kt_count - 2) % 3, grid, stream);
-    }
+    launch_peel<EPI, OUT_BF16, kRing>(g, (kt_count - (kRing - 1)) % kRing, grid, stream);
 }
 
 template <int EPI>
