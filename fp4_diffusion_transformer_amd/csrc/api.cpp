@@ -153,7 +153,8 @@ fp4dit_status fp4dit_gemm_fp4_epilogue_swiglu(int64_t M, int64_t N, int64_t K, c
     if (N % (2 * fp4dit::kSwigluGroup) != 0) return FP4DIT_E_SHAPE;
     if (M == 0) return FP4DIT_OK;
     if (!out && !out_codes) return FP4DIT_E_NULL;
-    if ((out && !aligned(out, 16)) || (out_codes && !aligned(out_codes, 16))) return FP4DIT_E_ALIGN;
+    if ((out && !aligned(out, 16)) || (out_codes && (!aligned(out_codes, 16) || !aligned(out_scales, 2))))
+        return FP4DIT_E_ALIGN;
     return launched(fp4dit::launch_gemm_swiglu(M, N, K, a_codes, a_scales, b_codes, b_scales, out,
                                                out_dtype == FP4DIT_BF16, out_codes, out_scales, stream));
 }

@@ -23,20 +23,20 @@ typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- e8m0 ----
 // Shared exponent of a block from the bits of its largest magnitude.
-// Returns the e8m0 byte (shared + 127); 0xFF when amax is Inf or NaN.
+// Returns the e8m0 byte (shared + 127); 0xFF when amax is Inf or NaN, 0 for
+// an all-zero block.  Branch-free (selects only).
 __device__ __forceinline__ uint32_t e8m0_from_amax_bits(uint32_t amax_bits) {
-    if (amax_bits >= 0x7F800000u) return 0xFFu;          // Inf / NaN: unsupported
-    if (amax_bits == 0u) return 0u;                      // all-zero block
     const uint32_t e = amax_bits >> 23;
-    int floor_log2;
-    if (e != 0u) {
-        floor_log2 = (int)e - 127;
-    } else {                                             // subnormal amax
-        floor_log2 = (31 - __builtin_clz(amax_bits)) - 149;
-    }
+    // floor(log2 amax): from the exponent field, or for a subnormal amax
+    // from the position of its leading one (value = bits * 2^-149)
+    const int normal = (int)e - 127;
+    const int subnormal = (31 - (int)__builtin_clz(amax_bits | 1u)) - 149;
+    const int pick = -(int)(e != 0u);                   // all ones for a normal amax
+    const int floor_log2 = (normal & pick) | (subnormal & ~pick);
     int shared = floor_log2 - 2;
     shared = shared < -127 ? -127 : (shared > 127 ? 127 : shared);
-    return (uint32_t)(shared + 127);
+    const uint32_t s = (uint32_t)(shared + 127);
+    return amax_bits >= 0x7F800000u ? 0xFFu : (amax_bits == 0u ? 0u : s);
 }
 
 // --------------------------------------------------------------- e2m1 -----

@@ -140,12 +140,13 @@ __device__ __forceinline__ uint32_t opaque_sgpr(uint32_t x) {
     return x;
 }
 
-// A per-lane 32-bit value the compiler may not hoist: values derived from
-// it are recomputed where used instead of being kept live (or spilled)
-// across the whole tile loop.
-__device__ __forceinline__ uint32_t opaque_vgpr(uint32_t x) {
-    asm volatile("" : "+v"(x));
-    return x;
+// This lane's index in the wave (v_mbcnt over the full mask), recomputed at
+// every call: per-lane values derived from it are formed where they are used
+// instead of being kept live (and spilled) across the whole tile loop.
+__device__ __forceinline__ int fresh_lane_id() {
+    uint32_t l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return (int)l;
 }
 
 // Per-lane byte offsets of the direct-to-LDS loads, fixed for the K loop (the
@@ -169,9 +170,8 @@ __device__ __forceinline__ uint32_t scale_tile_off(uint32_t r, uint32_t kq) {
 // one instruction moves 16 rows x 64 B (lane: row lane/4, 16-byte chunk
 // lane%4, written at its swizzled position), the scale instructions 64 rows
 // x 4 B.
-__device__ __forceinline__ LoadPlan make_plan(int M, int K, int n0, int m0, int wave, int lane_) {
+__device__ __forceinline__ LoadPlan make_plan(int M, int K, int n0, int m0, int wave, int lane) {
     LoadPlan p;
-    const int lane = (int)opaque_vgpr((uint32_t)lane_);
     const uint32_t kq = (uint32_t)(K / 128);            // K stages (tiles per row pair / row block)
     const int rin = lane >> 2;                          // row within a 16-row group
     const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);  // chunk for physical slot lane & 3
@@ -435,10 +435,13 @@ __device__ __forceinline__ void k_stage(v16f (&acc)[4][4], Frags& f0, Frags& f1,
 // 256-wide head (both channel halves) are exchanged through its last 2 KiB.
 // acc[nb][mb][i]: channel n0 + wn*128 + nb*32 + 8*(i/4) + 4h + i%4,
 //                 token   m0 + wm*128 + mb*32 + r32.
-template <int EPI, bool OUT_BF16>
+// after_mb(mb) runs once the outputs of token block mb are stored (it issues
+// the next tile's prefetch in pieces, so that the stores are not queued
+// behind all of it).
+template <int EPI, bool OUT_BF16, typename AfterMb>
 __device__ __forceinline__ void epilogue(v16f (&acc)[4][4], const GemmArgs& g, int64_t n0, int64_t m0,
-                                         uint8_t* stg, int wave, int lane_) {
-    const int lane = (int)opaque_vgpr((uint32_t)lane_);
+                                         uint8_t* stg, int wave, AfterMb after_mb) {
+    const int lane = fresh_lane_id();
     const int wn = wave & 1, wm = wave >> 1;
     const int r32 = lane & 31, h = lane >> 5;
     const int64_t cbase = n0 + wn * 128;
@@ -508,6 +511,7 @@ __device__ __forceinline__ void epilogue(v16f (&acc)[4][4], const GemmArgs& g, i
                     }
                 }
             }
+            after_mb(mb);
         }
     }
 
@@ -542,6 +546,13 @@ __device__ __forceinline__ void epilogue(v16f (&acc)[4][4], const GemmArgs& g, i
                 }
             }
             if (g.out_codes != nullptr) {
+                // Requant of the two 32-output blocks b = ob0/32 + p (p = 0, 1)
+                // of token tok: lane h gathers block b + h whole (16 bytes,
+                // half of its codes from the partner lane l ^ 32) and stores
+                // it with one 16-byte store; lanes h = 0 store both scale
+                // bytes (adjacent in the tiled layout, b even) as one u16.
+                uint32_t sc[2];
+                uint32_t c16[2][4];                   // [p][a]: codes of outputs 8a+4h .. +3
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
                     uint32_t amax = 0u;
@@ -550,38 +561,39 @@ __device__ __forceinline__ void epilogue(v16f (&acc)[4][4], const GemmArgs& g, i
                         const uint32_t a = __float_as_uint(hv[p][i]) & 0x7FFFFFFFu;
                         amax = a > amax ? a : amax;
                     }
-                    amax = max_xor32_u(amax);
-                    const uint32_t sc = e8m0_from_amax_bits(amax);
-                    uint32_t c16[4];                  // codes of outputs 8a+4h .. +3
+                    sc[p] = e8m0_from_amax_bits(max_xor32_u(amax));
 #pragma unroll
-                    for (int a = 0; a < 4; ++a) c16[a] = sc == 0xFFu ? 0u : e2m1_pack4(&hv[p][4 * a], sc);
-                    // lane h=0 stores bytes 0..7 of the block (outputs 0..15),
-                    // lane h=1 bytes 8..15; each needs two halves from its partner.
-                    const uint32_t send = h == 0 ? (c16[2] | (c16[3] << 16)) : (c16[0] | (c16[1] << 16));
-                    const uint32_t recv = partner_xor32(send, lane);
-                    v2u st;
-                    if (h == 0) {
-                        st[0] = c16[0] | ((recv & 0xFFFFu) << 16);
-                        st[1] = c16[1] | ((recv >> 16) << 16);
-                    } else {
-                        st[0] = (recv & 0xFFFFu) | (c16[2] << 16);
-                        st[1] = (recv >> 16) | (c16[3] << 16);
-                    }
-                    if (tok < g.M) {                  // MX_TILED output, ready for the next GEMM
-                        const int64_t blk = ob0 / 32 + p;
-                        *reinterpret_cast<v2u*>(g.out_codes + tiled_code_off(tok, blk * 32, nh) + h * 8) = st;
-                        if (h == 0) g.out_scales[tiled_scale_off(tok, blk, nh)] = (uint8_t)sc;
+                    for (int a = 0; a < 4; ++a) {
+                        const uint32_t c = e2m1_pack4(&hv[p][4 * a], sc[p]);
+                        c16[p][a] = sc[p] == 0xFFu ? 0u : c;   // Inf / NaN block: zero codes
                     }
                 }
+                // lane h keeps block h and sends block 1 - h (two dwords)
+                const uint32_t send0 = h == 0 ? (c16[1][0] | (c16[1][1] << 16)) : (c16[0][0] | (c16[0][1] << 16));
+                const uint32_t send1 = h == 0 ? (c16[1][2] | (c16[1][3] << 16)) : (c16[0][2] | (c16[0][3] << 16));
+                const uint32_t recv0 = partner_xor32(send0, lane);
+                const uint32_t recv1 = partner_xor32(send1, lane);
+                const uint32_t rc[4] = {recv0 & 0xFFFFu, recv0 >> 16, recv1 & 0xFFFFu, recv1 >> 16};
+                v4u st;                                // dword a: outputs 8a .. 8a+7 of block b + h
+#pragma unroll
+                for (int a = 0; a < 4; ++a) st[a] = h == 0 ? (c16[0][a] | (rc[a] << 16)) : (rc[a] | (c16[1][a] << 16));
+                if (tok < g.M) {                       // MX_TILED output, ready for the next GEMM
+                    const int64_t blk = ob0 / 32;
+                    *reinterpret_cast<v4u*>(g.out_codes + tiled_code_off(tok, (blk + h) * 32, nh)) = st;
+                    if (h == 0)
+                        *reinterpret_cast<uint16_t*>(g.out_scales + tiled_scale_off(tok, blk, nh)) =
+                            (uint16_t)(sc[0] | (sc[1] << 8));
+                }
             }
+            after_mb(mb);
         }
     }
 }
 
 // Persistent kernel: workgroup b runs tiles b, b + G, b + 2G, ... (G = grid
 // size, a multiple of 8 so every tile of one workgroup maps to its own XCD).
-// While a tile's epilogue runs, the first NS - 1 K stages of the next tile
-// are already loading into the other ring slots.
+// The first NS - 1 K stages of the next tile load while the current tile's
+// epilogue runs, one stage after each of its first token blocks is stored.
 // NS: ring depth (kRing); PEEL: (K/128 - NS + 1) % NS, the stages run before
 // the unrolled loop.
 template <int EPI, bool OUT_BF16, int NS, int PEEL>
@@ -592,13 +604,9 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(1024))) uint8_t ring2[NS > 2 ? kStageBytes : 16];
     __shared__ __attribute__((aligned(1024))) uint8_t ring3[NS > 3 ? kStageBytes : 16];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int wn = wave & 1;              // channel half of the workgroup tile (128 channels)
     const int wm = wave >> 1;             // token half (128 tokens)
-    const int r32 = lane & 31;
-    const int h = lane >> 5;
     const int M = (int)g.M, K = (int)g.K;    // M * K / 2 < 2^31 (checked by the host)
     const int tiles_n = (int)(g.N / kBN);
     const int tiles_m = (M + kBM - 1) / kBM;
@@ -621,12 +629,18 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
     int v = blockIdx.x;
     int tm, tn;
     tile_of(v, n_tiles, tiles_n, tiles_m, tm, tn);
-    LoadPlan plan = make_plan(M, K, tn * kBN, tm * kBM, wave, lane);
-    static_for<0, D>([&](auto j) { issue_stage_at(slots[(j() + OFF) % NS], ops, plan, j(), wave); });
+    {
+        const LoadPlan plan = make_plan(M, K, tn * kBN, tm * kBM, wave, fresh_lane_id());
+        static_for<0, D>([&](auto j) { issue_stage_at(slots[(j() + OFF) % NS], ops, plan, j(), wave); });
+    }
 
     for (;;) {
         const int n0 = tn * kBN;
         const int m0 = tm * kBM;
+        const int lane = fresh_lane_id();
+        const int r32 = lane & 31;
+        const int h = lane >> 5;
+        const LoadPlan plan = make_plan(M, K, n0, m0, wave, lane);
         v16f acc[4][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -664,12 +678,15 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
 
         const int vn = v + (int)gridDim.x;
         const bool more = vn < n_tiles;
-        if (more) {                                    // prefetch the next tile, then finish this one
-            tile_of(vn, n_tiles, tiles_n, tiles_m, tm, tn);
-            plan = make_plan(M, K, tn * kBN, tm * kBM, wave, lane);
-            static_for<0, D>([&](auto j) { issue_stage_at(slots[(j() + OFF) % NS], ops, plan, j(), wave); });
-        }
-        epilogue<EPI, OUT_BF16>(acc, g, n0, m0, stg, wave, lane);
+        if (more) tile_of(vn, n_tiles, tiles_n, tiles_m, tm, tn);
+        // finish this tile; after its token block j (< D) is stored, stage j
+        // of the next tile starts loading (its load offsets are formed there
+        // rather than kept live through the epilogue)
+        epilogue<EPI, OUT_BF16>(acc, g, n0, m0, stg, wave, [&](int mb) {
+            if (more && mb < D)
+                issue_stage_at(slots[(mb + OFF) % NS], ops, make_plan(M, K, tn * kBN, tm * kBM, wave, fresh_lane_id()),
+                               mb, wave);
+        });
         if (!more) break;
         v = vn;
     }

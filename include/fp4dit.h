@@ -225,8 +225,8 @@ fp4dit_status fp4dit_gemm_fp4_epilogue_rmsnorm_head(int64_t M, int64_t N, int64_
  * out        NULL, or [M][N/2] of out_dtype (16-byte aligned).
  * out_codes, out_scales  both NULL, or both set: MXFP4 re-quantisation of
  *            the fp32 h [M][N/2] along its columns, in the MX_TILED layout
- *            (ready to be the A operand of the next GEMM; codes 16-byte
- *            aligned), encoded as fp4dit_quantize_mxfp4 does.
+ *            (ready to be the A operand of the next GEMM; codes 16-byte,
+ *            scales 2-byte aligned), encoded as fp4dit_quantize_mxfp4 does.
  * At least one output must be set.
  */
 fp4dit_status fp4dit_gemm_fp4_epilogue_swiglu(int64_t M, int64_t N, int64_t K,
