@@ -8,61 +8,75 @@
 //
 // Activation quantisation is HBM-bound: 2 (bf16) or 4 (fp32) bytes in and
 // 17/32 byte out per element.  Four lanes share a 32-element block; each
-// lane loads 8 consecutive elements (16 B of bf16), so a wave reads 1 KiB of
-// contiguous memory per load and writes 256 contiguous bytes of codes.  The
-// block amax is reduced over the four lanes with DPP quad permutes.
+// lane takes 8 consecutive elements (16 B of bf16), so a wave reads 1 KiB of
+// contiguous memory per load.  A thread handles kUnits such 8-element units
+// 256 units apart and issues all their loads before using any, so that
+// enough bytes are in flight per CU to cover the HBM latency; the input is
+// read once (non-temporal loads).  The block amax is reduced over the four
+// lanes with DPP quad permutes.
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace fp4dit {
 
+constexpr int kQuantUnits = 4;                   // 8-element units per thread
+
 template <bool kBf16, bool kTiled>
 __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ x,
                                                        uint8_t* __restrict__ codes,
                                                        uint8_t* __restrict__ scales,
-                                                       int64_t nblocks, int64_t cols) {
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t blk = gid >> 2;
-    const int part = (int)(gid & 3);
-    if (blk >= nblocks) return;                  // whole quads leave together
-    uint32_t xb[8];
-    const int64_t elem = blk * 32 + part * 8;
-    if (kBf16) {
-        const v4u v = *reinterpret_cast<const v4u*>(static_cast<const uint16_t*>(x) + elem);
+                                                       int64_t nunits, int64_t cols) {
+    uint32_t xb[kQuantUnits][8];
+    int64_t unit[kQuantUnits];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            xb[2 * i] = v[i] << 16;
-            xb[2 * i + 1] = v[i] & 0xFFFF0000u;
-        }
-    } else {
-        const v4u* p = reinterpret_cast<const v4u*>(static_cast<const float*>(x) + elem);
-        const v4u v0 = p[0], v1 = p[1];
+    for (int i = 0; i < kQuantUnits; ++i) {
+        unit[i] = ((int64_t)blockIdx.x * kQuantUnits + i) * 256 + threadIdx.x;
+        if (unit[i] >= nunits) continue;         // whole quads leave together (nunits % 4 == 0)
+        const int64_t elem = unit[i] * 8;
+        if (kBf16) {
+            const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(static_cast<const uint16_t*>(x) + elem));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            xb[i] = v0[i];
-            xb[4 + i] = v1[i];
+            for (int j = 0; j < 4; ++j) {
+                xb[i][2 * j] = v[j] << 16;
+                xb[i][2 * j + 1] = v[j] & 0xFFFF0000u;
+            }
+        } else {
+            const v4u* p = reinterpret_cast<const v4u*>(static_cast<const float*>(x) + elem);
+            const v4u v0 = __builtin_nontemporal_load(p), v1 = __builtin_nontemporal_load(p + 1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                xb[i][j] = v0[j];
+                xb[i][4 + j] = v1[j];
+            }
         }
     }
-    uint32_t amax = 0u;
+    const int part = (int)(threadIdx.x & 3);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t a = xb[i] & 0x7FFFFFFFu;
-        amax = a > amax ? a : amax;
-    }
-    amax = max_quad_u(amax);
-    const uint32_t sc = e8m0_from_amax_bits(amax);
-    float xf[8];
+    for (int i = 0; i < kQuantUnits; ++i) {
+        if (unit[i] >= nunits) continue;
+        const int64_t blk = unit[i] >> 2;
+        uint32_t amax = 0u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xf[i] = __uint_as_float(xb[i]);
-    const uint32_t w = sc == 0xFFu ? 0u : e2m1_pack8(xf, sc);
-    if (kTiled) {
-        const uint32_t nbr = (uint32_t)(cols >> 5);              // blocks per row (nblocks < 2^32)
-        const uint32_t row = (uint32_t)blk / nbr, b = (uint32_t)blk - row * nbr;
-        *reinterpret_cast<uint32_t*>(codes + tiled_code_off(row, (int64_t)b * 32 + part * 8, cols)) = w;
-        if (part == 0) scales[tiled_scale_off(row, b, cols)] = (uint8_t)sc;
-    } else {
-        reinterpret_cast<uint32_t*>(codes)[blk * 4 + part] = w;
-        if (part == 0) scales[blk] = (uint8_t)sc;
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t a = xb[i][j] & 0x7FFFFFFFu;
+            amax = a > amax ? a : amax;
+        }
+        amax = max_quad_u(amax);
+        const uint32_t sc = e8m0_from_amax_bits(amax);
+        float xf[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xf[j] = __uint_as_float(xb[i][j]);
+        const uint32_t enc = e2m1_pack8(xf, sc);
+        const uint32_t w = sc == 0xFFu ? 0u : enc;   // Inf / NaN block: zero codes
+        if (kTiled) {
+            const uint32_t nbr = (uint32_t)(cols >> 5);              // blocks per row (nblocks < 2^32)
+            const uint32_t row = (uint32_t)blk / nbr, b = (uint32_t)blk - row * nbr;
+            *reinterpret_cast<uint32_t*>(codes + tiled_code_off(row, (int64_t)b * 32 + part * 8, cols)) = w;
+            if (part == 0) scales[tiled_scale_off(row, b, cols)] = (uint8_t)sc;
+        } else {
+            reinterpret_cast<uint32_t*>(codes)[unit[i]] = w;
+            if (part == 0) scales[blk] = (uint8_t)sc;
+        }
     }
 }
 
@@ -114,11 +128,11 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const void* __restrict
 
 hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols,
                            uint8_t* codes, uint8_t* scales, bool tiled, hipStream_t stream) {
-    const int64_t nblocks = rows * (cols / 32);
-    const int64_t threads = nblocks * 4;
-    const dim3 grid((unsigned)((threads + 255) / 256));
+    const int64_t nunits = rows * (cols / 32) * 4;
+    const int64_t per_wg = 256 * kQuantUnits;
+    const dim3 grid((unsigned)((nunits + per_wg - 1) / per_wg));
 #define FP4DIT_Q(B, T) \
-    hipLaunchKernelGGL((quantize_kernel<B, T>), grid, dim3(256), 0, stream, x, codes, scales, nblocks, cols)
+    hipLaunchKernelGGL((quantize_kernel<B, T>), grid, dim3(256), 0, stream, x, codes, scales, nunits, cols)
     if (bf16) {
         if (tiled) FP4DIT_Q(true, true); else FP4DIT_Q(true, false);
     } else {

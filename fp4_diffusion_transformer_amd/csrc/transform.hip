@@ -7,8 +7,9 @@
 // activations are split into independent 32-element blocks with one learned
 // matrix each, which turns the transform into small-tile matrix-core GEMMs.
 //
-// Online kernel (HBM-bound): one wave owns 32 tokens x 4 consecutive blocks
-// (128 channels, so each token row is read as 256 contiguous bytes).  Per
+// Online kernel (HBM-bound): one wave owns 4 consecutive blocks (128
+// channels) of 4 x 32 tokens; each 32-token group is staged in LDS by
+// direct-to-LDS loads of whole rows (double-buffered, see issue_group).  Per
 // block it runs two bf16 MFMAs V_MFMA_F32_32X32X16_BF16 computing
 // Y_b^T = T_b^T . X_b^T, i.e. lane l ends with token l%32 and output
 // features 8a + 4(l/32) + r (a, r = 0..3) -- the same accumulator layout as
@@ -56,20 +57,61 @@ __device__ __forceinline__ void store_mx_block(const float* hv, int lane, bool l
 
 constexpr int kTokIters = 4;           // 32-token groups per wave
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt, expcnt, lgkmcnt.
+constexpr int waitcnt_imm(int vm, int exp, int lgkm) {
+    return (vm & 15) | ((exp & 7) << 4) | ((lgkm & 15) << 8) | (((vm >> 4) & 3) << 14);
+}
+
+// Loads of a 32-token group: each wave stages its 32 tokens x 128 channels
+// (4 blocks) in its own LDS buffer with direct-to-LDS loads.  One load moves
+// 64 x 16 B = whole rows (4 of bf16, 2 of fp32), i.e. full cache lines; in
+// LDS the 16-byte chunk c of row r sits at c ^ (r & 15), so that the operand
+// reads below (lane = token row, fixed chunk) hit 16 different chunk
+// positions per quarter-wave: no bank conflicts.  Rows past the last token
+// and chunks past the last column are clamped to valid memory (never used).
+template <int kEsz>
+__device__ __forceinline__ void issue_group(uint8_t* buf, const void* x, int64_t rows, int64_t cols,
+                                            int64_t tok0, int64_t b0, int lane) {
+    constexpr int kChunks = 128 * kEsz / 16;             // 16-byte chunks per token row
+    constexpr int kLoads = 32 * kChunks / 64;            // loads per group
+    constexpr int kPerChunk = 16 / kEsz;                 // elements per chunk
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) {
+        const int row = q * (64 / kChunks) + lane / kChunks;
+        const int logical = (lane % kChunks) ^ (row & 15);
+        int64_t tok = tok0 + row;
+        tok = tok < rows ? tok : rows - 1;
+        int64_t ch = b0 * 32 + logical * kPerChunk;
+        ch = ch < cols ? ch : cols - kPerChunk;
+        const uint8_t* src = static_cast<const uint8_t*>(x) + (tok * cols + ch) * kEsz;
+        __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + q * 1024), 16, 0, 0);
+    }
+}
+
 template <bool kXBf16, bool kYBf16, bool kTiled>
 __global__ __launch_bounds__(256) void block_transform_kernel(const void* __restrict__ x, int64_t rows,
                                                               int64_t cols, const uint16_t* __restrict__ t,
                                                               int64_t n_t, void* __restrict__ y,
                                                               uint8_t* __restrict__ codes,
                                                               uint8_t* __restrict__ scales) {
+    constexpr int kEsz = kXBf16 ? 2 : 4;
+    constexpr int kRowBytes = 128 * kEsz;                // 4 blocks of one token
+    constexpr int kBufBytes = 32 * kRowBytes;            // one 32-token group (8 / 16 KiB)
+    constexpr int kLoads = kBufBytes / 1024;
+    __shared__ __attribute__((aligned(1024))) uint8_t stage[4][2][kBufBytes];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int h = lane >> 5;
     const int r32 = lane & 31;
     const int64_t nblk = cols / 32;
     const int64_t b0 = ((int64_t)blockIdx.x * 4 + wave) * 4;   // first of this wave's 4 blocks
-    if (b0 >= nblk) return;                                     // wave-uniform
+    if (b0 >= nblk) return;                                     // wave-uniform; no workgroup barriers below
     const int64_t tok_base = (int64_t)blockIdx.y * (32 * kTokIters);
+    uint8_t* const bufs[2] = {stage[wave][0], stage[wave][1]};
+
+    issue_group<kEsz>(bufs[0], x, rows, cols, tok_base, b0, lane);
 
     // A operand: lane holds T_b^T row r32 (= column r32 of T_b) at
     // k = 8h..8h+7 (first MFMA) and 16 + 8h.. (second MFMA).
@@ -84,33 +126,50 @@ __global__ __launch_bounds__(256) void block_transform_kernel(const void* __rest
             for (int e = 0; e < 8; ++e) tf[j][half][e] = (short)tb[(16 * half + 8 * h + e) * 32 + r32];
     }
 
+#pragma unroll
     for (int it = 0; it < kTokIters; ++it) {
+        const uint8_t* buf = bufs[it & 1];
+        if (it + 1 < kTokIters) {
+            // the other buffer was last read in iteration it - 1 (those reads
+            // completed before their MFMAs): refill it with the next group
+            issue_group<kEsz>(bufs[(it + 1) & 1], x, rows, cols, tok_base + (it + 1) * 32, b0, lane);
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(kLoads, 7, 15));     // this group's loads landed
+        } else {
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 7, 15));
+        }
+        asm volatile("" ::: "memory");
         const int64_t tok = tok_base + it * 32 + r32;
         const bool live = tok < rows;
-        const int64_t trow = live ? tok : rows - 1;
+        const uint8_t* row = buf + r32 * kRowBytes;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t b = b0 + j;
             if (b >= nblk) break;                                   // wave-uniform
+            // B operand: features 16 half + 8h .. +7 of block j for token r32
             v8s xf[2];
-            const int64_t e0 = trow * cols + b * 32;
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                const int64_t e = e0 + 16 * half + 8 * h;
+                const int g = 2 * half + h;                         // 8-feature group in the block
                 if (kXBf16) {
-                    const v4u v = *reinterpret_cast<const v4u*>(static_cast<const uint16_t*>(x) + e);
+                    const int c = (4 * j + g) ^ (r32 & 15);
+                    const v4u v = *reinterpret_cast<const v4u*>(row + c * 16);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         xf[half][2 * i] = (short)(v[i] & 0xFFFFu);
                         xf[half][2 * i + 1] = (short)(v[i] >> 16);
                     }
                 } else {
-                    const v4f* p = reinterpret_cast<const v4f*>(static_cast<const float*>(x) + e);
-                    const v4f v0 = p[0], v1 = p[1];
+                    const int c0 = (8 * j + 2 * g) ^ (r32 & 15), c1 = (8 * j + 2 * g + 1) ^ (r32 & 15);
+                    const v4f v0 = *reinterpret_cast<const v4f*>(row + c0 * 16);
+                    const v4f v1 = *reinterpret_cast<const v4f*>(row + c1 * 16);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        xf[half][i] = (short)f32_to_bf16_bits(v0[i]);
-                        xf[half][4 + i] = (short)f32_to_bf16_bits(v1[i]);
+                    for (int i = 0; i < 2; ++i) {
+                        const uint32_t p0 = pack_bf16x2(v0[2 * i], v0[2 * i + 1]);
+                        const uint32_t p1 = pack_bf16x2(v1[2 * i], v1[2 * i + 1]);
+                        xf[half][2 * i] = (short)(p0 & 0xFFFFu);
+                        xf[half][2 * i + 1] = (short)(p0 >> 16);
+                        xf[half][4 + 2 * i] = (short)(p1 & 0xFFFFu);
+                        xf[half][4 + 2 * i + 1] = (short)(p1 >> 16);
                     }
                 }
             }
