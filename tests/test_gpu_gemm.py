@@ -165,3 +165,34 @@ def test_swiglu_requant(with_bf16):
     scales = layout.untile_scales(host(mx.scales), mx.rows, mx.cols)
     exc_codes, exc_blocks = parity.assert_codes_banded(codes, scales, h_ref, "swiglu requant")
     assert exc_codes <= 0.001 * h_ref.size
+
+
+@pytest.mark.parametrize("epilogue", ["none", "rmsnorm", "swiglu_requant"])
+def test_persistent_many_tiles_ragged(epilogue):
+    """More 256 x 256 tiles (4 x 80 = 320) than a persistent grid holds, so
+    workgroups run several tiles in turn (the next tile's loads overlapping
+    the epilogue), with a ragged last token tile (1000 = 3 * 256 + 232)."""
+    rng = np.random.default_rng(31)
+    m, n, k = 1000, 256 * 80, 512
+    rows = np.unique(np.concatenate([[0, 255, 256, 767, 768, 999], rng.choice(m, 40, replace=False)]))
+    announce("gemm persistent", epilogue, m, n, k)
+    if epilogue == "swiglu_requant":
+        operands, h_ref = _swiglu_operands(rng, m, n // 2, k)
+        _, mx = ops.gemm_fp4_epilogue_swiglu(*_dev_ops(*operands), out_dtype=None, requant=True)
+        codes = layout.untile_codes(host(mx.codes), mx.rows, mx.cols)
+        scales = layout.untile_scales(host(mx.scales), mx.rows, mx.cols)
+        exc, _ = parity.assert_codes_banded(codes[rows], scales[rows], h_ref[rows], "persistent swiglu requant")
+        assert exc <= 0.001 * h_ref[rows].size
+        return
+    ac, as_, bc, bs = _operands(rng, m, n, k)
+    c = ogemm.gemm(ac[rows], as_[rows], bc, bs)
+    if epilogue == "none":
+        out = ops.gemm_fp4_epilogue_none(*_dev_ops(ac, as_, bc, bs), out_dtype=torch.float32)
+        parity.assert_close(host(out)[rows], c, parity.TOL_F32, what="persistent none")
+    else:
+        n_norm = n - 2048
+        norm_w = rng.uniform(0.5, 1.5, n_norm).astype(np.float32)
+        ref = ogemm.rmsnorm_head(c, 128, n_norm, norm_w.astype(np.float64), 1e-6)
+        out = ops.gemm_fp4_epilogue_rmsnorm_head(*_dev_ops(ac, as_, bc, bs), 128, n_norm,
+                                                 dev(norm_w, torch.float32), 1e-6, out_dtype=torch.bfloat16)
+        parity.assert_close(host(out)[rows], ref, parity.TOL_BF16, group=128, what="persistent rmsnorm")
