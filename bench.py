@@ -40,6 +40,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--warm-seconds", type=float, default=0.5,
+                   help="untimed steps run for this long before the warmup steps: under a sustained FP4 "
+                        "MFMA load the GPU's clock settles within tens of milliseconds, and a timed region "
+                        "that starts from idle reads 10-15%% slow")
     p.add_argument("--workload", default="dit_1k_linears", choices=["dit_1k_linears", "dit_block"])
     p.add_argument("--rotate", type=int, default=4, help="activation buffer copies cycled over steps")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -247,6 +251,13 @@ def main():
             if ev is not None and i == dom:
                 ev["g1"][s].record()
 
+    t_warm = time.perf_counter()
+    s = 0
+    while time.perf_counter() - t_warm < args.warm_seconds:
+        step(s)
+        s += 1
+        if s % 20 == 0:
+            torch.cuda.synchronize()
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()

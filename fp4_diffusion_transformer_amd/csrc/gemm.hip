@@ -67,6 +67,7 @@ constexpr int kRedOff = 0;
 static_assert(4 * kStageOutBytes <= kStageBytes && kRedOff + 2 * kBM * 4 <= kStageBytes,
               "epilogue LDS does not fit");
 constexpr int kDmaPerStage = 10;       // direct-to-LDS instructions per wave per stage
+constexpr int kDmaEarly = 8;           // of them issued before the stage's barrier
 
 enum EpiKind { kEpiNone = 0, kEpiRmsNorm = 1, kEpiSwiglu = 2 };
 
@@ -379,14 +380,15 @@ __device__ __forceinline__ void read_scale(uint32_t* wsc, uint32_t* xsc, const u
 
 // One K stage of the main loop on ring slot `cur`, scheduled by hand (each
 // sched_barrier pins the instructions issued since the previous one):
-// * K-step 0: MFMA n on the fragments read one step earlier, with load n of
-//   stage kt + kRing - 1 (n < 10, ISSUE) and the read of second-step
-//   fragment n (n < 8);
+// * K-step 0: MFMA n on the fragments read one step earlier, with (ISSUE)
+//   load n/2 of stage kt + kRing - 1 on every even n -- kDmaEarly loads --
+//   and the read of second-step fragment n (n < 8);
 // * barrier (NEXT): this wave's stage-kt+1 loads landed (at most VM loads
 //   remain in flight) and every wave is done with stage kt;
-// * K-step 1: the 8 scale and 8 fragment reads of stage kt+1 go out with the
-//   first 8 MFMAs, so that they have landed long before K-step 0 of the next
-//   stage needs them.
+// * K-step 1: the last kDmaPerStage - kDmaEarly loads go out with MFMAs 6..,
+//   and the 8 scale then 8 fragment reads of stage kt+1 one per MFMA.
+// Measured against packing the loads into the first 10 slots, reads into the
+// first 8 of K-step 1, or loading after the barrier: about 2% faster.
 template <bool ISSUE, bool NEXT, int VM>
 __device__ __forceinline__ void k_stage(v16f (&acc)[4][4], Frags& f0, Frags& f1, uint32_t* wsc, uint32_t* xsc,
                                         uint8_t* cur_, uint8_t* nxt_, uint8_t* fill, const Operands& ops,
@@ -402,7 +404,7 @@ __device__ __forceinline__ void k_stage(v16f (&acc)[4][4], Frags& f0, Frags& f1,
     static_for<0, 16>([&](auto n) {
         constexpr int kN = decltype(n)::value;
         mfma_one<0>(acc[kN / 4][kN % 4], f0.w[kN / 4], f0.x[kN % 4], wsc[kN / 4], xsc[kN % 4]);
-        if constexpr (ISSUE && kN < 10) issue_load(kN, fill_codes, fill_scales, ops, plan, soff);
+        if constexpr (ISSUE && kN % 2 == 0) issue_load(kN / 2, fill_codes, fill_scales, ops, plan, soff);
         if constexpr (kN < 8) read_frag<kN>(f1, cur, wn, wm, r32, h, 1);
         __builtin_amdgcn_sched_barrier(0);
     });
@@ -411,11 +413,14 @@ __device__ __forceinline__ void k_stage(v16f (&acc)[4][4], Frags& f0, Frags& f1,
     static_for<0, 16>([&](auto n) {
         constexpr int kN = decltype(n)::value;
         mfma_one<1>(acc[kN / 4][kN % 4], f1.w[kN / 4], f1.x[kN % 4], wsc[kN / 4], xsc[kN % 4]);
-        if constexpr (kN < 8) {
-            if (NEXT) {
+        constexpr int kLate = kN - 6;                          // late loads in slots 6, 7
+        if constexpr (ISSUE && kLate >= 0 && kLate < kDmaPerStage - kDmaEarly)
+            issue_load(kDmaEarly + kLate, fill_codes, fill_scales, ops, plan, soff);
+        if (NEXT) {
+            if constexpr (kN < 8)
                 read_scale<kN>(wsn, xsn, nxt, wn, wm, r32, h);
-                read_frag<kN>(f0, nxt, wn, wm, r32, h, 0);
-            }
+            else
+                read_frag<kN - 8>(f0, nxt, wn, wm, r32, h, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
     });
@@ -621,7 +626,11 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
     // tile's prefetch leaves free for the epilogue.
     constexpr int D = NS - 1;                          // prefetch distance (stages)
     constexpr int OFF = (NS - PEEL) % NS;
-    constexpr int kVmSteady = (D - 1) * kDmaPerStage;  // loads allowed in flight at a barrier
+    // loads that may still be in flight at a barrier: in the K loop, those of
+    // the D - 1 later stages issued before it; at a tile's start, the whole
+    // prefetched stages after stage 0
+    constexpr int kVmSteady = (D - 1) * kDmaEarly;
+    constexpr int kVmPrologue = (D - 1) * kDmaPerStage;
     uint8_t* const slots[4] = {ring0, ring1, ring2, ring3};
     uint8_t* const stg = slots[(OFF + D) % NS];
     const int n_issue = kt_count - D;
@@ -647,7 +656,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = (v16f){};
 
-        ring_barrier<kVmSteady>();                     // stage 0 landed
+        ring_barrier<kVmPrologue>();                   // stage 0 landed
         Frags f0, f1;
         uint32_t wsc[4], xsc[4];
         read_scales(wsc, xsc, slots[OFF % NS], wn, wm, r32, h);
