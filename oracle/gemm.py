@@ -19,11 +19,18 @@ definitions written out; the GPU reaches them up to fp32 accumulation order.
   at packing time so that gate and up columns become neighbours.  The oracle
   computes from the logical (un-permuted) halves, so its result does not
   depend on the permutation.
+* SwiGLU -> block transform -> MXFP4 (the same page's point that an epilogue
+  saves the output's HBM round trip, applied to the FFN's down projection,
+  whose input is transformed block by block before quantisation per the
+  KroQuant page, "Background and overview" and "Deep analysis"): the SwiGLU
+  output h is multiplied, 32 columns at a time, by the down layer's T_b and
+  the product is quantised.  Reading: h is carried unrounded between the
+  steps (as the re-quantisation takes h itself, not a bf16 copy of it).
 """
 
 import numpy as np
 
-from . import mxfp4
+from . import mxfp4, transform
 
 
 def gemm(a_codes, a_scales, b_codes, b_scales):
@@ -108,3 +115,9 @@ def swiglu_from_interleaved(c_phys, group):
 def requantize(h, return_scaled=False):
     """MXFP4 re-quantisation of an epilogue output along its columns."""
     return mxfp4.quantize(h, return_scaled=return_scaled)
+
+
+def swiglu_transform_requantize(c_gate, c_up, t, return_scaled=False):
+    """h = SwiGLU(gate, up); y = h block-transformed by T (y_b = h_b @ T_b);
+    MXFP4 codes and scales of y, all in float64 with h unrounded."""
+    return mxfp4.quantize(transform.block_transform(swiglu(c_gate, c_up), t), return_scaled=return_scaled)

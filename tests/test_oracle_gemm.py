@@ -162,3 +162,68 @@ def test_interleaved_swiglu_equals_split_halves(g):
     halves = gemm.silu(full[:, :n_half]) * full[:, n_half:]
     assert np.allclose(ref, halves, rtol=1e-13, atol=1e-13)
     assert np.allclose(gemm.swiglu_from_interleaved(c_phys, g), halves, rtol=1e-12, atol=1e-12)
+
+
+# SwiGLU -> block transform -> MXFP4 (the down projection's input, fused)
+
+def _gate_up_without_zeros(rng, m, n):
+    g = rng.standard_normal((m, n)) * 2.0
+    u = rng.standard_normal((m, n)) * 2.0
+    g[g == 0] = 0.5
+    u[u == 0] = 0.5
+    return g, u
+
+
+@pytest.mark.parametrize("n_t", [1, 3])
+def test_swiglu_transform_identity_is_requant(n_t):
+    rng = np.random.default_rng(40 + n_t)
+    g, u = _gate_up_without_zeros(rng, 6, 96)
+    t = np.broadcast_to(np.eye(32), (n_t, 32, 32)).copy()
+    c1, s1 = gemm.swiglu_transform_requantize(g, u, t)
+    c2, s2 = mxfp4.quantize(g / (1.0 + np.exp(-g)) * u)     # SiLU(g) * u written out
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+
+
+def test_swiglu_transform_signed_permutation():
+    """A signed permutation per block moves and sign-flips the codes of h
+    exactly and keeps every block scale; a transposed T, another block's T,
+    or T applied to the gate or up alone would not."""
+    rng = np.random.default_rng(44)
+    g, u = _gate_up_without_zeros(rng, 8, 64)
+    h = g / (1.0 + np.exp(-g)) * u
+    t = np.zeros((2, 32, 32))
+    perms, signs = [], []
+    for b in range(2):
+        perm = rng.permutation(32)
+        sign = rng.choice([-1.0, 1.0], 32)
+        t[b, perm, np.arange(32)] = sign                 # y_j = h_perm[j] * s_j
+        perms.append(perm)
+        signs.append(sign)
+    c_t, s_t = gemm.swiglu_transform_requantize(g, u, t)
+    c_h, s_h = mxfp4.quantize(h)
+    assert np.array_equal(s_t, s_h)
+    for b in range(2):
+        src = c_h[:, 32 * b:32 * b + 32][:, perms[b]]
+        flip = np.broadcast_to((signs[b] < 0).astype(np.uint8) << 3, src.shape)
+        assert np.array_equal(c_t[:, 32 * b:32 * b + 32], src ^ flip)
+
+
+def test_swiglu_transform_keeps_h_unrounded():
+    """h just above an e2m1 rounding midpoint, by less than bf16 resolution:
+    the code rounds up.  (A bf16 copy of h would sit on the midpoint and
+    round to even, i.e. down.)  Block scale fixed by an element of 5.5 * 2^s."""
+    s = -3
+    targets = [5.5, 0.25 + 2.0 ** -12, 1.25 + 2.0 ** -10, 2.5 + 2.0 ** -9]   # scaled values q
+    want = [7, 1, 3, 5]                                   # codes of 6, 0.5, 1.5, 3
+    g = np.full((1, 32), 3.0)
+    silu_g = 3.0 / (1.0 + np.exp(-3.0))
+    q = np.full(32, 0.5)
+    q[:4] = targets
+    u = (q * 2.0 ** s / silu_g)[None]
+    c, sc = gemm.swiglu_transform_requantize(g, u, np.eye(32)[None])
+    assert sc[0, 0] == 127 + s
+    assert list(c[0, :4]) == want
+    # the same values rounded to bf16 first land on midpoints and round to even
+    hb = bf16.round_bf16(g / (1.0 + np.exp(-g)) * u)
+    cb, _ = mxfp4.quantize(hb)
+    assert list(cb[0, 1:4]) == [0, 2, 4]

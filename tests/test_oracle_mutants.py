@@ -42,6 +42,13 @@ def _pins_gemm():
         tg.test_interleaved_swiglu_equals_split_halves(g)
 
 
+def _pins_fused():
+    for n_t in (1, 3):
+        tg.test_swiglu_transform_identity_is_requant(n_t)
+    tg.test_swiglu_transform_signed_permutation()
+    tg.test_swiglu_transform_keeps_h_unrounded()
+
+
 def _pins_transform():
     tt.test_identity_transform_gives_plain_codes()
     tt.test_signed_permutation_permutes_codes()
@@ -173,6 +180,20 @@ def _bf16_truncate(x):
     return ((f.view(np.uint32) >> 16).astype(np.uint16))
 
 
+def _fused_h_via_bf16(c_gate, c_up, t, return_scaled=False):
+    h = bf16.round_bf16(gemm.swiglu(c_gate, c_up))
+    return mxfp4.quantize(transform.block_transform(h, t), return_scaled=return_scaled)
+
+
+def _fused_transform_on_gate(c_gate, c_up, t, return_scaled=False):
+    return mxfp4.quantize(gemm.swiglu(transform.block_transform(c_gate, t), c_up), return_scaled=return_scaled)
+
+
+def _fused_transform_transposed(c_gate, c_up, t, return_scaled=False):
+    t = np.swapaxes(np.asarray(t, dtype=np.float64), 1, 2)
+    return mxfp4.quantize(transform.block_transform(gemm.swiglu(c_gate, c_up), t), return_scaled=return_scaled)
+
+
 MUTANTS = [
     ("ties_round_up", mxfp4, "encode_magnitude", _ties_up, _pins_mxfp4),
     ("ties_round_down", mxfp4, "encode_magnitude", _ties_down, _pins_mxfp4),
@@ -192,6 +213,10 @@ MUTANTS = [
     ("transform_transposed", transform, "block_transform", _transform_transposed, _pins_transform),
     ("fold_transposed", transform, "fold_inverse", _fold_transposed, _pins_transform),
     ("bf16_truncates", bf16, "to_bf16_bits", _bf16_truncate, _pins_gemm),
+    ("fused_h_rounded_to_bf16", gemm, "swiglu_transform_requantize", _fused_h_via_bf16, _pins_fused),
+    ("fused_transform_on_gate", gemm, "swiglu_transform_requantize", _fused_transform_on_gate, _pins_fused),
+    ("fused_transform_transposed", gemm, "swiglu_transform_requantize", _fused_transform_transposed,
+     _pins_fused),
 ]
 
 
@@ -206,3 +231,4 @@ def test_pins_pass_unmutated():
     _pins_mxfp4()
     _pins_gemm()
     _pins_transform()
+    _pins_fused()
