@@ -15,6 +15,10 @@ Workloads (seeded synthetic tensors, random-init weights):
   dit_block                 batch of 4 images (16384 tokens): block transform +
                             quantise of every input, QKV (RMSNorm hd 128), FFN up
                             (SwiGLU, bf16 out), FFN down (no epilogue).
+  dit_block_fused           the same block with the down projection's input made
+                            in the FFN-up epilogue: SwiGLU -> down transform ->
+                            MXFP4, so h never reaches HBM and the down layer has
+                            no transform + quantise pass of its own.
 
 Prints one JSON line.  TFLOP/s counts 2*M*N*K per GEMM (N the physical width).
 """
@@ -44,7 +48,7 @@ def parse():
                    help="untimed steps run for this long before the warmup steps: under a sustained FP4 "
                         "MFMA load the GPU's clock settles within tens of milliseconds, and a timed region "
                         "that starts from idle reads 10-15%% slow")
-    p.add_argument("--workload", default="dit_1k_linears", choices=["dit_1k_linears", "dit_block"])
+    p.add_argument("--workload", default="dit_1k_linears", choices=["dit_1k_linears", "dit_block", "dit_block_fused"])
     p.add_argument("--rotate", type=int, default=4, help="activation buffer copies cycled over steps")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calib-mib", type=int, default=0,
@@ -90,8 +94,12 @@ class Layer:
             self.norm_w = torch.from_numpy(wl.norm_w).to(dev, torch.float32)
         self.flops = 2 * self.m * self.n * self.k
         self.ops = ops
+        self.next_t = None          # set: SwiGLU -> this block transform -> MXFP4 into next_a
+        self.next_a = None
 
     def quantize(self, step):
+        if self.xs is None:         # activations made by the previous layer's epilogue
+            return
         x = self.xs[step % len(self.xs)]
         if self.t is not None:
             self.ops.block_transform(x, self.t, quantize=True, out=self.a)
@@ -103,6 +111,8 @@ class Layer:
         if wl.epilogue == "rmsnorm_head":
             ops.gemm_fp4_epilogue_rmsnorm_head(self.a, self.b, wl.head_dim, wl.n_norm, self.norm_w, wl.eps,
                                                out=self.out)
+        elif wl.epilogue == "swiglu" and self.next_t is not None:
+            ops.gemm_fp4_epilogue_swiglu_transform(self.a, self.b, self.next_t, out_mx=self.next_a)
         elif wl.epilogue == "swiglu":
             ops.gemm_fp4_epilogue_swiglu(self.a, self.b, out_dtype=None, requant=wl.requant, out=self.out,
                                          out_mx=self.req)
@@ -111,6 +121,8 @@ class Layer:
 
     def quant_bytes(self):
         """Algorithmic HBM bytes of the activation quantiser: bf16 in, codes + scales out."""
+        if self.xs is None:
+            return 0
         return self.m * self.k * 2 + self.m * self.k // 2 + self.m * self.k // 32
 
     def gemm_bytes(self):
@@ -118,7 +130,8 @@ class Layer:
         ab = self.m * self.k // 2 + self.m * self.k // 32
         bb = self.n * self.k // 2 + self.n * self.k // 32
         if self.wl.epilogue == "swiglu":
-            ob = self.m * (self.n // 4 + self.n // 64) if self.wl.requant else self.m * self.n
+            ob = self.m * (self.n // 4 + self.n // 64) if (self.wl.requant or self.next_t is not None) \
+                else self.m * self.n
         else:
             ob = self.m * self.n * 2
         return ab + bb + ob
@@ -138,7 +151,13 @@ def build_layers(args, ops, torch, workloads):
     up_layer.out = torch.empty((up_layer.m, n_half), dtype=torch.bfloat16, device="cuda")
     up_layer.req = None
     dl = Layer("dit_block_down", down, ops, torch, 1, transform=down.t)
-    dl.xs = [up_layer.out]                                         # chained: the up layer's bf16 output
+    if args.workload == "dit_block_fused":
+        # The up epilogue writes the down layer's MXFP4 activations directly.
+        up_layer.out = None
+        up_layer.next_t, up_layer.next_a = dl.t, dl.a
+        dl.xs = None
+    else:
+        dl.xs = [up_layer.out]                                     # chained: the up layer's bf16 output
     layers.append(dl)
     return layers
 
@@ -298,7 +317,8 @@ def main():
     # depth (3) and the K stages peeled before its unrolled loop
     out_bf16 = Ld.out is not None
     kt, ring = Ld.k // 128, 3
-    kernel_key = "gemm_%s<%s,%d,%d>" % (Ld.wl.epilogue, "true" if out_bf16 else "false", ring, (kt - ring + 1) % ring)
+    epi_name = Ld.wl.epilogue + ("_transform" if Ld.next_t is not None else "")
+    kernel_key = "gemm_%s<%s,%d,%d>" % (epi_name, "true" if out_bf16 else "false", ring, (kt - ring + 1) % ring)
 
     out = {
         "metric": "fused MXFP4 GEMM+epilogue TFLOPS and % of MXFP4 peak at DiT 1K shapes",
@@ -316,7 +336,10 @@ def main():
         "config": {
             "workload": args.workload,
             "layers": [{"name": L.name, "M": L.m, "N": L.n, "K": L.k, "epilogue": L.wl.epilogue
-                        + ("+requant" if L.wl.requant else "") + ("+transform" if L.t is not None else "")}
+                        + ("+requant" if L.wl.requant else "")
+                        + ("+next_transform+requant" if L.next_t is not None else ""),
+                        "input": "block transform + quantise" if L.t is not None and L.xs is not None
+                        else ("from the previous epilogue" if L.xs is None else "quantise")}
                        for L in layers],
             "pct_of_mxfp4_peak": round(100.0 * tflops / PEAK_MXFP4_TFLOPS, 2),
             "wall_s_timed": round(wall, 3),

@@ -159,4 +159,24 @@ fp4dit_status fp4dit_gemm_fp4_epilogue_swiglu(int64_t M, int64_t N, int64_t K, c
                                                out_dtype == FP4DIT_BF16, out_codes, out_scales, stream));
 }
 
+fp4dit_status fp4dit_gemm_fp4_epilogue_swiglu_transform(int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                                                        const uint8_t* a_scales, const uint8_t* b_codes,
+                                                        const uint8_t* b_scales, const uint16_t* t_bf16,
+                                                        int64_t n_t, void* y, fp4dit_dtype y_dtype,
+                                                        uint8_t* out_codes, uint8_t* out_scales,
+                                                        hipStream_t stream) {
+    if (y && !valid_dtype(y_dtype)) return FP4DIT_E_UNSUPPORTED;
+    const fp4dit_status st = check_gemm(M, N, K, a_codes, a_scales, b_codes, b_scales);
+    if (st != FP4DIT_OK) return st;
+    if (N % (2 * fp4dit::kSwigluGroup) != 0) return FP4DIT_E_SHAPE;
+    if (n_t != 1 && n_t != N / 64) return FP4DIT_E_SHAPE;
+    if (M == 0) return FP4DIT_OK;
+    if (!t_bf16 || !out_codes || !out_scales) return FP4DIT_E_NULL;
+    if ((y && !aligned(y, 16)) || !aligned(t_bf16, 2) || !aligned(out_codes, 16) || !aligned(out_scales, 2))
+        return FP4DIT_E_ALIGN;
+    return launched(fp4dit::launch_gemm_swiglu_transform(M, N, K, a_codes, a_scales, b_codes, b_scales, t_bf16,
+                                                         n_t, y, y_dtype == FP4DIT_BF16, out_codes, out_scales,
+                                                         stream));
+}
+
 }  // extern "C"

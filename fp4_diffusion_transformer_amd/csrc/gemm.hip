@@ -69,7 +69,7 @@ static_assert(4 * kStageOutBytes <= kStageBytes && kRedOff + 2 * kBM * 4 <= kSta
 constexpr int kDmaPerStage = 10;       // direct-to-LDS instructions per wave per stage
 constexpr int kDmaEarly = 8;           // of them issued before the stage's barrier
 
-enum EpiKind { kEpiNone = 0, kEpiRmsNorm = 1, kEpiSwiglu = 2 };
+enum EpiKind { kEpiNone = 0, kEpiRmsNorm = 1, kEpiSwiglu = 2, kEpiSwigluTransform = 3 };
 
 struct GemmArgs {
     int64_t M, N, K;
@@ -86,7 +86,12 @@ struct GemmArgs {
     // swiglu requant
     uint8_t* out_codes;
     uint8_t* out_scales;
+    // block transform of the SwiGLU output before the requant: T [n_t][32][32]
+    const uint16_t* t;
+    int64_t n_t;
 };
+
+typedef short v8s __attribute__((ext_vector_type(8)));
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -433,6 +438,52 @@ __device__ __forceinline__ void k_stage(v16f (&acc)[4][4], Frags& f0, Frags& f1,
     }
 }
 
+// Block transform inside the SwiGLU epilogue (KroQuant, "Deep analysis": the
+// next layer's input is transformed 32 features at a time, y_b = h_b . T_b).
+// Per 32-token x 32-feature block of h it is Y^T = T_b^T . H^T on
+// V_MFMA_F32_32X32X16_BF16, two MFMAs over the 32 input features.  The
+// contraction order is free, so each lane feeds its own 16 values of h as
+// they sit in the accumulator layout (features 8a + 4h + r): MFMA s takes
+// hv[8s .. 8s+7] as K slots 8h .. 8h+7, i.e. slot 16s + 8h + e carries
+// feature 16s + 8(e/4) + 4h + e%4, and the A operand (lane = output feature
+// r32) is gathered from T_b's rows in the same order.  The result has the
+// accumulator layout again, ready for the requant.  h is fp32 and the MFMA
+// takes bf16, so h is split into hi = bf16(h) and lo = bf16(h - hi) and both
+// parts are multiplied (h - hi - lo is below 2^-16 |h|).
+__device__ __forceinline__ void load_t_frags(v8s (&tf)[2][2], const GemmArgs& g, int64_t blk0, int r32, int h) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const uint16_t* tb = g.t + (g.n_t == 1 ? 0 : (blk0 + p) * 1024) + r32;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tf[p][s][e] = (short)tb[(16 * s + 8 * (e / 4) + 4 * h + e % 4) * 32];
+    }
+}
+
+__device__ __forceinline__ void transform_block(float* hv, const v8s (&tf)[2]) {
+    v8s hi[2], lo[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const float a = hv[8 * s + e], b = hv[8 * s + e + 1];
+            const uint32_t ph = pack_bf16x2(a, b);
+            const uint32_t pl = pack_bf16x2(a - bf16_bits_to_f32(ph & 0xFFFFu), b - bf16_bits_to_f32(ph >> 16));
+            hi[s][e] = (short)(ph & 0xFFFFu);
+            hi[s][e + 1] = (short)(ph >> 16);
+            lo[s][e] = (short)(pl & 0xFFFFu);
+            lo[s][e + 1] = (short)(pl >> 16);
+        }
+    v16f y = {};
+    y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[0], lo[0], y, 0, 0, 0);
+    y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[1], lo[1], y, 0, 0, 0);
+    y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[0], hi[0], y, 0, 0, 0);
+    y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[1], hi[1], y, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) hv[i] = y[i];
+}
+
 // Epilogue of one tile: per-head RMSNorm / SwiGLU (+ MXFP4 requant) / plain
 // cast on the accumulators, then the single store.  `stg` is the LDS ring
 // slot left free by the next tile's prefetch: each wave stages its bf16
@@ -520,12 +571,14 @@ __device__ __forceinline__ void epilogue(v16f (&acc)[4][4], const GemmArgs& g, i
         }
     }
 
-    if (EPI == kEpiSwiglu) {
+    if (EPI == kEpiSwiglu || EPI == kEpiSwigluTransform) {
         // Channel blocks alternate gate / up (interleave group 32): block 2p
         // of the wave holds gate outputs and block 2p+1 the matching up
         // outputs cbase/2 + 32p + 8a + 4h + r.
         const int64_t nh = g.N / 2;
         const int64_t ob0 = cbase / 2;
+        v8s tf[2][2];
+        if (EPI == kEpiSwigluTransform) load_t_frags(tf, g, ob0 / 32, r32, h);
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
             float hv[2][16];                  // [p][4a + r]
@@ -533,6 +586,10 @@ __device__ __forceinline__ void epilogue(v16f (&acc)[4][4], const GemmArgs& g, i
             for (int p = 0; p < 2; ++p)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) hv[p][i] = silu_f(acc[2 * p][mb][i]) * acc[2 * p + 1][mb][i];
+            if (EPI == kEpiSwigluTransform) {
+#pragma unroll
+                for (int p = 0; p < 2; ++p) transform_block(hv[p], tf[p]);
+            }
             const int64_t tok = tok0 + mb * 32 + r32;
             if (g.out != nullptr) {
                 if (OUT_BF16) {
@@ -749,7 +806,8 @@ hipError_t launch_gemm(const GemmArgs& g, int epi, bool out_bf16, hipStream_t st
     switch (epi) {
         case kEpiNone: launch_epi<kEpiNone>(g, out_bf16, grid, stream); break;
         case kEpiRmsNorm: launch_epi<kEpiRmsNorm>(g, out_bf16, grid, stream); break;
-        default: launch_epi<kEpiSwiglu>(g, out_bf16, grid, stream); break;
+        case kEpiSwiglu: launch_epi<kEpiSwiglu>(g, out_bf16, grid, stream); break;
+        default: launch_epi<kEpiSwigluTransform>(g, out_bf16, grid, stream); break;
     }
     return hipGetLastError();
 }
@@ -787,6 +845,19 @@ hipError_t launch_gemm_swiglu(int64_t M, int64_t N, int64_t K, const uint8_t* ac
     g.out = out;
     g.out_codes = out_codes; g.out_scales = out_scales;
     return launch_gemm(g, kEpiSwiglu, out_bf16, stream);
+}
+
+hipError_t launch_gemm_swiglu_transform(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                                        const uint8_t* bc, const uint8_t* bs, const uint16_t* t, int64_t n_t,
+                                        void* out, bool out_bf16, uint8_t* out_codes, uint8_t* out_scales,
+                                        hipStream_t stream) {
+    GemmArgs g{};
+    g.M = M; g.N = N; g.K = K;
+    g.a_codes = ac; g.a_scales = as; g.b_codes = bc; g.b_scales = bs;
+    g.out = out;
+    g.out_codes = out_codes; g.out_scales = out_scales;
+    g.t = t; g.n_t = n_t;
+    return launch_gemm(g, kEpiSwigluTransform, out_bf16, stream);
 }
 
 }  // namespace fp4dit

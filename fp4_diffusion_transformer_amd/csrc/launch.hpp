@@ -34,6 +34,11 @@ hipError_t launch_gemm_swiglu(int64_t M, int64_t N, int64_t K, const uint8_t* ac
                               const uint8_t* bc, const uint8_t* bs, void* out, bool out_bf16,
                               uint8_t* out_codes, uint8_t* out_scales, hipStream_t stream);
 
+hipError_t launch_gemm_swiglu_transform(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                                        const uint8_t* bc, const uint8_t* bs, const uint16_t* t, int64_t n_t,
+                                        void* out, bool out_bf16, uint8_t* out_codes, uint8_t* out_scales,
+                                        hipStream_t stream);
+
 // Interleave group of the SwiGLU epilogue: channel blocks of 32 alternate
 // gate / up, matching one 32x32 MFMA output block per half.
 constexpr int kSwigluGroup = 32;

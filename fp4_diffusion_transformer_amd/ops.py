@@ -53,6 +53,7 @@ def lib():
             "fp4dit_gemm_fp4_epilogue_none": [I64, I64, I64, P, P, P, P, P, I32, P],
             "fp4dit_gemm_fp4_epilogue_rmsnorm_head": [I64, I64, I64, P, P, P, P, I32, I64, P, F, P, I32, P],
             "fp4dit_gemm_fp4_epilogue_swiglu": [I64, I64, I64, P, P, P, P, P, I32, P, P, P],
+            "fp4dit_gemm_fp4_epilogue_swiglu_transform": [I64, I64, I64, P, P, P, P, P, I64, P, I32, P, P, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -242,3 +243,22 @@ def gemm_fp4_epilogue_swiglu(a: MxTensor, b: MxTensor, out_dtype=torch.bfloat16,
           _ptr(b.scales), _ptr(h), _dtype_code(h.dtype) if h is not None else F32,
           _ptr(mx.codes) if mx else None, _ptr(mx.scales) if mx else None, _stream())
     return h, mx
+
+
+def gemm_fp4_epilogue_swiglu_transform(a: MxTensor, b: MxTensor, t, y_dtype=None, y=None,
+                                       out_mx: Optional[MxTensor] = None):
+    """SwiGLU over an interleaved weight, block-transformed by t (bfloat16
+    [n_t, 32, 32], y_b = h_b @ T_b) and quantised.  Returns (y or None,
+    MxTensor): y [M, N/2] when y_dtype (or `y`) is given, and the tiled MXFP4
+    encoding of y (into `out_mx` if given)."""
+    m, n, k = _gemm_shapes(a, b)
+    _dev(t, "t")
+    if t.dtype != torch.bfloat16:
+        raise ValueError("t must be bfloat16")
+    if y is None and y_dtype is not None:
+        y = torch.empty((m, n // 2), dtype=y_dtype, device=a.codes.device)
+    mx = out_mx if out_mx is not None else mx_empty(m, n // 2, "tiled", a.codes.device)
+    _call("fp4dit_gemm_fp4_epilogue_swiglu_transform", m, n, k, _ptr(a.codes), _ptr(a.scales), _ptr(b.codes),
+          _ptr(b.scales), _ptr(t), t.shape[0], _ptr(y), _dtype_code(y.dtype) if y is not None else F32,
+          _ptr(mx.codes), _ptr(mx.scales), _stream())
+    return y, mx

@@ -46,7 +46,7 @@ def kernel_key(name):
     """Short key of a kernel name (template arguments kept)."""
     n = name.replace("fp4dit::(anonymous namespace)::", "").replace("fp4dit::", "")
     for a, b in (("gemm_fp4_kernel<0,", "gemm_none<"), ("gemm_fp4_kernel<1,", "gemm_rmsnorm_head<"),
-                 ("gemm_fp4_kernel<2,", "gemm_swiglu<")):
+                 ("gemm_fp4_kernel<2,", "gemm_swiglu<"), ("gemm_fp4_kernel<3,", "gemm_swiglu_transform<")):
         n = n.replace(a, b)
     return n.split("(")[0].replace("void ", "").replace(" ", "").strip()
 

@@ -236,6 +236,33 @@ fp4dit_status fp4dit_gemm_fp4_epilogue_swiglu(int64_t M, int64_t N, int64_t K,
                                               uint8_t* out_codes, uint8_t* out_scales,
                                               hipStream_t stream);
 
+/*
+ * SwiGLU epilogue carried through the next layer's block transform and
+ * quantised (fal, "Fusing gated SiLU" and the epilogue-fusion section: the
+ * output makes no HBM round trip; KroQuant, "Background and overview" and
+ * "Deep analysis": the down projection's input is transformed per 32-element
+ * block before it is quantised).  With h [M][N/2] as in
+ * fp4dit_gemm_fp4_epilogue_swiglu (same B packing and constraints on N):
+ *     y[m][32b + j] = sum_i h[m][32b + i] * T_b[i][j]
+ * computed from the fp32 h (not a bf16 copy of it; the product is formed
+ * from bf16 parts h = hi + lo with fp32 accumulation, so its error is below
+ * 2^-16 of sum_i |h_i T_b[i][j]|), then MXFP4-quantised along its columns.
+ * t_bf16     [n_t][32][32] bfloat16 bit patterns, row i = input feature,
+ *            2-byte aligned; n_t = 1 (one T for every block) or N/64.
+ * y          NULL, or [M][N/2] of y_dtype (16-byte aligned): y itself.
+ * out_codes, out_scales  required: MXFP4 codes / scales of y in the
+ *            MX_TILED layout (codes 16-byte, scales 2-byte aligned), ready
+ *            to be the A operand of the down-projection GEMM, whose weights
+ *            carry the inverse transform (fp4dit_fold_inverse_transform).
+ */
+fp4dit_status fp4dit_gemm_fp4_epilogue_swiglu_transform(int64_t M, int64_t N, int64_t K,
+                                                        const uint8_t* a_codes, const uint8_t* a_scales,
+                                                        const uint8_t* b_codes, const uint8_t* b_scales,
+                                                        const uint16_t* t_bf16, int64_t n_t,
+                                                        void* y, fp4dit_dtype y_dtype,
+                                                        uint8_t* out_codes, uint8_t* out_scales,
+                                                        hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

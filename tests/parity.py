@@ -19,7 +19,9 @@ must match exactly.
 
 import numpy as np
 
+from oracle import gemm as ogemm
 from oracle import mxfp4
+from oracle import transform as otransform
 
 TAU = 1e-4
 AMAX_REL = 1e-5
@@ -63,25 +65,47 @@ def assert_codes_exact(gpu_packed, gpu_scales, ref_codes, ref_scales, what=""):
         what, len(bad), bad[0], gc[tuple(bad[0])], ref_codes[tuple(bad[0])])
 
 
-def _near_midpoint(q):
+def _near_midpoint(q, tau=TAU):
     a = np.abs(q)
     near = np.zeros(a.shape, dtype=bool)
     for mid in mxfp4.E2M1_MIDPOINTS:
-        near |= np.abs(a - mid) <= TAU
+        near |= np.abs(a - mid) <= tau
     return near
 
 
-def _near_pow2(amax):
+def split_product_bands(h, t, ref_scales):
+    """Bands for codes of y = h . T formed on the GPU from bf16 parts
+    h = hi + lo of an fp32 h: the neglected h - hi - lo is below 2^-16 |h|,
+    so |y_gpu - y| <= 2^-16 mag with mag_o = sum_i |h_i T_io|, on top of the
+    fp32 error that TAU and AMAX_REL cover.  h, t: the oracle's float64 h
+    and T.  Returns (tau per element in scaled units, amax_rel per block)."""
+    h = np.abs(np.asarray(h, dtype=np.float64))
+    t = np.abs(np.asarray(t, dtype=np.float64))
+    m, n = h.shape
+    mag = np.empty_like(h)
+    for b in range(n // 32):
+        mag[:, 32 * b:32 * b + 32] = h[:, 32 * b:32 * b + 32] @ (t[0] if t.shape[0] == 1 else t[b])
+    shared = np.repeat(np.asarray(ref_scales, dtype=np.float64) - 127.0, 32, axis=1)
+    tau = TAU + 2.0 ** -16 * mag / 2.0 ** shared
+    # amax >= 2^(shared + 2) for every block with a nonzero amax
+    blk_mag = np.max(mag.reshape(m, n // 32, 32), axis=2)
+    amax_rel = AMAX_REL + 2.0 ** -16 * blk_mag / 2.0 ** (np.asarray(ref_scales, dtype=np.float64) - 125.0)
+    return tau, amax_rel
+
+
+def _near_pow2(amax, amax_rel=AMAX_REL):
     with np.errstate(divide="ignore"):
         e = np.round(np.log2(np.where(amax > 0, amax, 1.0)))
-    return np.abs(amax / 2.0 ** e - 1.0) <= AMAX_REL
+    return np.abs(amax / 2.0 ** e - 1.0) <= amax_rel
 
 
-def assert_codes_banded(gpu_packed, gpu_scales, ref_values, what="", ref=None):
+def assert_codes_banded(gpu_packed, gpu_scales, ref_values, what="", ref=None, tau=TAU, amax_rel=AMAX_REL):
     """Codes of fp32 sums vs the float64 oracle values, with the excusal band.
 
     ref: optionally the oracle's mxfp4.quantize(ref_values, return_scaled=True)
-    if already computed.  Returns (excused_codes, excused_blocks) counts."""
+    if already computed; tau: the midpoint band, a scalar or one per element;
+    amax_rel: the power-of-two band of block amaxes, a scalar or one per block.
+    Returns (excused_codes, excused_blocks) counts."""
     ref_values = np.asarray(ref_values, dtype=np.float64)
     rc, rs, q = ref if ref is not None else mxfp4.quantize(ref_values, return_scaled=True)
     gc = unpack(gpu_packed)
@@ -89,13 +113,28 @@ def assert_codes_banded(gpu_packed, gpu_scales, ref_values, what="", ref=None):
     m, n = ref_values.shape
     amax = np.max(np.abs(ref_values.reshape(m, n // 32, 32)), axis=2)
     scale_bad = gs != rs
-    scale_ok_excuse = _near_pow2(amax)
+    scale_ok_excuse = _near_pow2(amax, amax_rel)
     unexcused_scale = scale_bad & ~scale_ok_excuse
     assert not unexcused_scale.any(), "%s: %d unexcused scale mismatches at %s" % (
         what, int(unexcused_scale.sum()), np.argwhere(unexcused_scale)[0])
     block_excused = np.repeat(scale_bad, 32, axis=1)
     code_bad = (gc != rc) & ~block_excused
-    unexcused = code_bad & ~_near_midpoint(q)
+    unexcused = code_bad & ~_near_midpoint(q, tau)
     assert not unexcused.any(), "%s: %d unexcused code mismatches, first %s (ref q=%r)" % (
         what, int(unexcused.sum()), np.argwhere(unexcused)[0], q[tuple(np.argwhere(unexcused)[0])])
     return int(code_bad.sum()), int(scale_bad.sum())
+
+
+def assert_fused_codes(gpu_codes, gpu_scales, c_gate, c_up, t, what=""):
+    """Unpacked-row codes / scales of the fused SwiGLU -> block transform ->
+    MXFP4 epilogue against the oracle's, from the oracle's accumulators
+    c_gate, c_up (float64) and T, with the split-product bands.  Returns
+    (h, y_ref, excused codes, excused blocks)."""
+    t64 = np.asarray(t, dtype=np.float64)
+    rc, rs, q = ogemm.swiglu_transform_requantize(c_gate, c_up, t64, return_scaled=True)
+    h = ogemm.swiglu(c_gate, c_up)
+    y_ref = otransform.block_transform(h, t64)
+    tau, amax_rel = split_product_bands(h, t64, rs)
+    exc, blk = assert_codes_banded(gpu_codes, gpu_scales, y_ref, what, ref=(rc, rs, q), tau=tau, amax_rel=amax_rel)
+    assert exc <= 0.002 * y_ref.size and blk <= 0.002 * rs.size, "%s: %d codes / %d blocks excused" % (what, exc, blk)
+    return h, y_ref, exc, blk

@@ -37,7 +37,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 10
     raw = ctypes.CDLL(ops.library_path())
     for n in names:
         assert hasattr(raw, n), n
@@ -96,6 +96,21 @@ def test_swiglu_validation(L):
     assert s(*args, None, BF16, None, None, None) == E_NULL                # no output at all
     assert s(*args, None, BF16, P, None, None) == E_UNSUP                  # codes without scales
     assert s(*args, P_ODD, BF16, None, None, None) == E_ALIGN
+
+
+def test_swiglu_transform_validation(L):
+    s = L.fp4dit_gemm_fp4_epilogue_swiglu_transform
+    args = (256, 512, 512, P, P, P, P)
+    assert s(*args, P, 3, None, F32, P, P, None) == E_SHAPE                # n_t not 1 or N/64
+    assert s(*args, None, 8, None, F32, P, P, None) == E_NULL              # no T (n_t = N/64)
+    assert s(*args, P, 1, None, F32, None, P, None) == E_NULL              # codes are required
+    assert s(*args, P, 1, None, F32, P, None, None) == E_NULL
+    assert s(*args, P_ODD, 1, None, F32, P, P, None) == E_ALIGN            # T is bf16
+    assert s(*args, P, 1, P_ODD, BF16, P, P, None) == E_ALIGN
+    assert s(*args, P, 1, None, F32, P, P_ODD, None) == E_ALIGN            # scales pair: 2 bytes
+    assert s(*args, P, 1, P, 9, P, P, None) == E_UNSUP
+    assert s(256, 320, 512, P, P, P, P, P, 1, None, F32, P, P, None) == E_SHAPE   # N % 256
+    assert s(0, 512, 512, None, None, None, None, None, 1, None, F32, None, None, None) == OK
 
 
 def test_transform_pack_fold_validation(L):

@@ -193,3 +193,31 @@ def test_dit_block_batch4_stages(stage):
         ref, group_cols = c, None
     torch.cuda.synchronize()
     parity.assert_close(host(out)[rows], ref, parity.TOL_BF16, group=group_cols, what="dit " + stage)
+
+
+def test_dit_block_up_fused_down_transform():
+    """The batch-4 block's FFN-up GEMM with SwiGLU, the down layer's block
+    transform (384 matrices) and MXFP4 fused in its epilogue, at full size
+    (16384 x 24576 x 3072) on the oracle's operand codes; sampled rows
+    against the oracle's SwiGLU -> transform -> quantise."""
+    _, up, down = _dit_block()
+    t_up = up.t.astype(np.float64)
+    announce("config dit_block up fused with the down transform", up.m, up.n, up.k)
+    ac, as_ = transform.transform_quantize(up.x.astype(np.float64), t_up)
+    wg = transform.fold_inverse(up.w_gate.astype(np.float64), t_up)
+    wu = transform.fold_inverse(up.w_up.astype(np.float64), t_up)
+    gc_, gs_ = mxfp4.quantize(wg.T)
+    uc_, us_ = mxfp4.quantize(wu.T)
+    del wg, wu
+    pair, is_up = ogemm.interleave_columns(gc_.shape[0], ops.swiglu_interleave_group())
+    bc = np.where(is_up[:, None], uc_[pair], gc_[pair])
+    bs = np.where(is_up[:, None], us_[pair], gs_[pair])
+    rows = _rows(up.m, n=16, seed=7)
+    c_g = ogemm.gemm(ac[rows], as_[rows], gc_, gs_)
+    c_u = ogemm.gemm(ac[rows], as_[rows], uc_, us_)
+    a_dev, b_dev = _mx_dev(ac, as_), _mx_dev(bc, bs)
+    del ac, as_, bc, bs
+    _, mx = ops.gemm_fp4_epilogue_swiglu_transform(a_dev, b_dev, dev(down.t, torch.bfloat16))
+    torch.cuda.synchronize()
+    codes, scales = _untile(mx)
+    parity.assert_fused_codes(codes[rows], scales[rows], c_g, c_u, down.t, "dit up fused down transform")

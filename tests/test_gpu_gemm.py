@@ -12,10 +12,11 @@ import torch
 import layout
 import parity
 from gpu_util import announce, dev, dev_u8, host
-from fp4_diffusion_transformer_amd import ops
+from fp4_diffusion_transformer_amd import ops, workloads
 from oracle import bf16 as obf16
 from oracle import gemm as ogemm
 from oracle import mxfp4
+from oracle import transform as otransform
 
 pytestmark = pytest.mark.gpu
 
@@ -121,7 +122,7 @@ def test_rmsnorm_eps_dominates_tiny_heads():
     parity.assert_close(host(out), ref, parity.TOL_F32, group=128, what="tiny heads")
 
 
-def _swiglu_operands(rng, m, n_half, k):
+def _swiglu_operands(rng, m, n_half, k, parts=False):
     x = rng.standard_normal((m, k)) * 2.0 ** rng.integers(-2, 3, (m, 1))
     wg = rng.standard_normal((k, n_half)) / np.sqrt(k) * 2
     wu = rng.standard_normal((k, n_half)) / np.sqrt(k)
@@ -135,6 +136,8 @@ def _swiglu_operands(rng, m, n_half, k):
     bs = np.where(is_up[:, None], us_[pair], gs_[pair])
     c_g = ogemm.gemm(ac, as_, gc_, gs_)
     c_u = ogemm.gemm(ac, as_, uc_, us_)
+    if parts:
+        return (ac, as_, bc, bs), c_g, c_u
     return (ac, as_, bc, bs), ogemm.swiglu(c_g, c_u)
 
 
@@ -196,3 +199,78 @@ def test_persistent_many_tiles_ragged(epilogue):
         out = ops.gemm_fp4_epilogue_rmsnorm_head(*_dev_ops(ac, as_, bc, bs), 128, n_norm,
                                                  dev(norm_w, torch.float32), 1e-6, out_dtype=torch.bfloat16)
         parity.assert_close(host(out)[rows], ref, parity.TOL_BF16, group=128, what="persistent rmsnorm")
+
+
+# SwiGLU -> down-projection block transform -> MXFP4, fused in the epilogue
+
+def _check_fused(mx, y, c_g, c_u, t, rows=None, what="fused"):
+    """Codes (and y, if stored) of the fused epilogue against the oracle's
+    SwiGLU -> transform -> quantise, on the given rows."""
+    if rows is None:
+        rows = np.arange(c_g.shape[0])
+    codes = layout.untile_codes(host(mx.codes), mx.rows, mx.cols)[rows]
+    scales = layout.untile_scales(host(mx.scales), mx.rows, mx.cols)[rows]
+    h_rows, y_ref, _, _ = parity.assert_fused_codes(codes, scales, c_g[rows], c_u[rows], t, what)
+    if y is not None:
+        yg = host(y)[rows].astype(np.float64)
+        parity.assert_close(yg, y_ref, parity.TOL_F32, what=what + " y")
+        # the split-product error bound itself, with slack for fp32 sums
+        mag = otransform.block_transform(np.abs(h_rows), np.abs(t.astype(np.float64)))
+        rms = np.sqrt(np.mean(y_ref ** 2, axis=1, keepdims=True))
+        assert np.all(np.abs(yg - y_ref) <= 2.0 ** -16 * mag + 1e-5 * rms), what + ": y outside the bound"
+
+
+@pytest.mark.parametrize("m,n_t", [(300, 8), (300, 1), (1, 8)])
+def test_swiglu_transform(m, n_t):
+    rng = np.random.default_rng(51 + m + n_t)
+    operands, c_g, c_u = _swiglu_operands(rng, m, 256, 512, parts=True)
+    t = workloads.transforms(60 + n_t, n_t)
+    announce("gemm swiglu transform", m, n_t)
+    y, mx = ops.gemm_fp4_epilogue_swiglu_transform(*_dev_ops(*operands), dev(t, torch.bfloat16),
+                                                   y_dtype=torch.float32)
+    _check_fused(mx, y, c_g, c_u, t, what="swiglu transform")
+
+
+def test_swiglu_transform_codes_only_and_bf16_y():
+    """Codes without y, and with a bf16 y: the codes do not depend on it."""
+    rng = np.random.default_rng(57)
+    operands, c_g, c_u = _swiglu_operands(rng, 300, 512, 768, parts=True)
+    t = workloads.transforms(61, 16)
+    announce("gemm swiglu transform codes only / bf16 y")
+    a, b = _dev_ops(*operands)
+    y0, mx0 = ops.gemm_fp4_epilogue_swiglu_transform(a, b, dev(t, torch.bfloat16))
+    assert y0 is None
+    _check_fused(mx0, None, c_g, c_u, t, what="swiglu transform codes")
+    y1, mx1 = ops.gemm_fp4_epilogue_swiglu_transform(a, b, dev(t, torch.bfloat16), y_dtype=torch.bfloat16)
+    # (the padding rows of the tiled buffers are never written: compare the rows)
+    assert np.array_equal(layout.untile_codes(host(mx0.codes), 300, 512),
+                          layout.untile_codes(host(mx1.codes), 300, 512))
+    assert np.array_equal(layout.untile_scales(host(mx0.scales), 300, 512),
+                          layout.untile_scales(host(mx1.scales), 300, 512))
+    h_ref = ogemm.swiglu(c_g, c_u)
+    parity.assert_close(host(y1), otransform.block_transform(h_ref, t.astype(np.float64)), parity.TOL_BF16,
+                        what="swiglu transform bf16 y")
+
+
+def test_swiglu_transform_identity_is_requant():
+    """T = I: the fused codes follow the plain SwiGLU requant of h."""
+    rng = np.random.default_rng(58)
+    operands, c_g, c_u = _swiglu_operands(rng, 300, 256, 512, parts=True)
+    t = np.eye(32, dtype=np.float32)[None]
+    announce("gemm swiglu transform identity")
+    _, mx = ops.gemm_fp4_epilogue_swiglu_transform(*_dev_ops(*operands), dev(t, torch.bfloat16))
+    _check_fused(mx, None, c_g, c_u, t, what="swiglu transform identity")
+
+
+def test_swiglu_transform_persistent_many_tiles_ragged():
+    """320 tiles on the persistent grid, ragged last token tile, one T per
+    block (n_t = 320)."""
+    rng = np.random.default_rng(59)
+    m, n, k = 1000, 256 * 80, 512
+    rows = np.unique(np.concatenate([[0, 255, 256, 767, 768, 999], rng.choice(m, 40, replace=False)]))
+    operands, c_g, c_u = _swiglu_operands(rng, m, n // 2, k, parts=True)
+    t = workloads.transforms(62, n // 64)
+    announce("gemm swiglu transform persistent", m, n, k)
+    y, mx = ops.gemm_fp4_epilogue_swiglu_transform(*_dev_ops(*operands), dev(t, torch.bfloat16),
+                                                   y_dtype=torch.float32)
+    _check_fused(mx, y, c_g, c_u, t, rows=rows, what="persistent swiglu transform")
