@@ -15,6 +15,10 @@ Workloads (seeded synthetic tensors, random-init weights):
   dit_block                 batch of 4 images (16384 tokens): block transform +
                             quantise of every input, QKV (RMSNorm hd 128), FFN up
                             (SwiGLU, bf16 out), FFN down (no epilogue).
+  dit_1k_linears_unfused    the DiT-1K linears without epilogue fusion: each GEMM
+                            stores bf16, then RMSNorm / SwiGLU run as launches of
+                            their own and the SwiGLU output is quantised by the
+                            activation quantiser (what the fused epilogues save).
   dit_block_fused           the same block with the down projection's input made
                             in the FFN-up epilogue: SwiGLU -> down transform ->
                             MXFP4, so h never reaches HBM and the down layer has
@@ -48,7 +52,8 @@ def parse():
                    help="untimed steps run for this long before the warmup steps: under a sustained FP4 "
                         "MFMA load the GPU's clock settles within tens of milliseconds, and a timed region "
                         "that starts from idle reads 10-15%% slow")
-    p.add_argument("--workload", default="dit_1k_linears", choices=["dit_1k_linears", "dit_block", "dit_block_fused"])
+    p.add_argument("--workload", default="dit_1k_linears", choices=["dit_1k_linears", "dit_1k_linears_unfused", "dit_block",
+                                                                 "dit_block_fused"])
     p.add_argument("--rotate", type=int, default=4, help="activation buffer copies cycled over steps")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calib-mib", type=int, default=0,
@@ -96,6 +101,14 @@ class Layer:
         self.ops = ops
         self.next_t = None          # set: SwiGLU -> this block transform -> MXFP4 into next_a
         self.next_a = None
+        self.unfused = False
+
+    def make_unfused(self, torch):
+        """GEMM with a bf16 store, then the epilogue as launches of its own."""
+        self.unfused = True
+        self.c = torch.empty((self.m, self.n), dtype=torch.bfloat16, device="cuda")
+        if self.wl.epilogue == "swiglu":
+            self.h = torch.empty((self.m, self.n // 2), dtype=torch.bfloat16, device="cuda")
 
     def quantize(self, step):
         if self.xs is None:         # activations made by the previous layer's epilogue
@@ -108,7 +121,9 @@ class Layer:
 
     def gemm(self):
         ops, wl = self.ops, self.wl
-        if wl.epilogue == "rmsnorm_head":
+        if self.unfused:
+            ops.gemm_fp4_epilogue_none(self.a, self.b, out=self.c)
+        elif wl.epilogue == "rmsnorm_head":
             ops.gemm_fp4_epilogue_rmsnorm_head(self.a, self.b, wl.head_dim, wl.n_norm, self.norm_w, wl.eps,
                                                out=self.out)
         elif wl.epilogue == "swiglu" and self.next_t is not None:
@@ -118,6 +133,28 @@ class Layer:
                                          out_mx=self.req)
         else:
             ops.gemm_fp4_epilogue_none(self.a, self.b, out=self.out)
+
+    def epilogue(self):
+        """The unfused epilogue launches (nothing when the GEMM fuses it)."""
+        if not self.unfused:
+            return
+        ops, wl = self.ops, self.wl
+        if wl.epilogue == "rmsnorm_head":
+            ops.rmsnorm_head(self.c, wl.head_dim, wl.n_norm, self.norm_w, wl.eps, out=self.out)
+        elif wl.epilogue == "swiglu":
+            ops.swiglu(self.c, ops.swiglu_interleave_group(), out=self.h)
+            if wl.requant:
+                ops.quantize_mxfp4(self.h, out=self.req)
+
+    def epilogue_bytes(self):
+        """Algorithmic HBM bytes of the unfused epilogue launches."""
+        mn = self.m * self.n
+        if self.wl.epilogue == "rmsnorm_head":
+            return 2 * mn + 2 * mn                          # bf16 C in, bf16 y out
+        b = 2 * mn + mn                                     # bf16 C in, bf16 h [M, N/2] out
+        if self.wl.requant:
+            b += mn + self.m * (self.n // 4 + self.n // 64)   # h in, codes + scales out
+        return b
 
     def quant_bytes(self):
         """Algorithmic HBM bytes of the activation quantiser: bf16 in, codes + scales out."""
@@ -129,7 +166,9 @@ class Layer:
         """Algorithmic HBM bytes of the fused GEMM: both MXFP4 operands once, output once."""
         ab = self.m * self.k // 2 + self.m * self.k // 32
         bb = self.n * self.k // 2 + self.n * self.k // 32
-        if self.wl.epilogue == "swiglu":
+        if self.unfused:
+            ob = self.m * self.n * 2
+        elif self.wl.epilogue == "swiglu":
             ob = self.m * (self.n // 4 + self.n // 64) if (self.wl.requant or self.next_t is not None) \
                 else self.m * self.n
         else:
@@ -138,9 +177,13 @@ class Layer:
 
 
 def build_layers(args, ops, torch, workloads):
-    if args.workload == "dit_1k_linears":
+    if args.workload in ("dit_1k_linears", "dit_1k_linears_unfused"):
         wls = [workloads.qkv_hd128(), workloads.qkv_hd256(), workloads.ffn_up_swiglu(requant=True)]
-        return [Layer(w.name, w, ops, torch, args.rotate) for w in wls]
+        layers = [Layer(w.name, w, ops, torch, args.rotate) for w in wls]
+        if args.workload == "dit_1k_linears_unfused":
+            for L in layers:
+                L.make_unfused(torch)
+        return layers
     qkv, up, down = workloads.dit_block()
     layers = [Layer("dit_block_qkv", qkv, ops, torch, args.rotate, transform=qkv.t),
               Layer("dit_block_up", up, ops, torch, args.rotate, transform=up.t)]
@@ -269,6 +312,7 @@ def main():
             L.gemm()
             if ev is not None and i == dom:
                 ev["g1"][s].record()
+            L.epilogue()
 
     t_warm = time.perf_counter()
     s = 0
@@ -315,9 +359,9 @@ def main():
     achieved = Ld.flops / (g_avg * 1e-3) / 1e12
     # kernel instantiation as rocprof names it: epilogue, bf16 output, LDS ring
     # depth (3) and the K stages peeled before its unrolled loop
-    out_bf16 = Ld.out is not None
+    out_bf16 = Ld.out is not None or Ld.unfused
     kt, ring = Ld.k // 128, 3
-    epi_name = Ld.wl.epilogue + ("_transform" if Ld.next_t is not None else "")
+    epi_name = "none" if Ld.unfused else Ld.wl.epilogue + ("_transform" if Ld.next_t is not None else "")
     kernel_key = "gemm_%s<%s,%d,%d>" % (epi_name, "true" if out_bf16 else "false", ring, (kt - ring + 1) % ring)
 
     out = {
@@ -336,7 +380,7 @@ def main():
         "config": {
             "workload": args.workload,
             "layers": [{"name": L.name, "M": L.m, "N": L.n, "K": L.k, "epilogue": L.wl.epilogue
-                        + ("+requant" if L.wl.requant else "")
+                        + ("+requant" if L.wl.requant else "") + (" (unfused)" if L.unfused else "")
                         + ("+next_transform+requant" if L.next_t is not None else ""),
                         "input": "block transform + quantise" if L.t is not None and L.xs is not None
                         else ("from the previous epilogue" if L.xs is None else "quantise")}
@@ -368,6 +412,22 @@ def main():
             "algorithmic_bytes": Lq.quant_bytes(),
         },
     }
+    if any(L.unfused for L in layers):
+        # each layer's separate epilogue launches, timed like the quantiser
+        epis = []
+        for L in layers:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(QUANT_BATCH):
+                L.epilogue()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / QUANT_BATCH
+            epis.append({"layer": L.name, "avg_ms": round(ms, 5), "bound": "hbm",
+                         "achieved_GBs": round(L.epilogue_bytes() / (ms * 1e-3) / 1e9, 1),
+                         "algorithmic_bytes": L.epilogue_bytes()})
+        out["unfused_epilogues"] = epis
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, [L.wl for L in layers])
     print(json.dumps(out), flush=True)

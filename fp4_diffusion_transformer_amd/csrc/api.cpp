@@ -179,4 +179,31 @@ fp4dit_status fp4dit_gemm_fp4_epilogue_swiglu_transform(int64_t M, int64_t N, in
                                                          stream));
 }
 
+fp4dit_status fp4dit_rmsnorm_head(const uint16_t* x, int64_t rows, int64_t cols, int32_t head_dim,
+                                  int64_t n_norm_cols, const float* norm_w, float eps, uint16_t* out,
+                                  hipStream_t stream) {
+    if (head_dim != 128 && head_dim != 256) return FP4DIT_E_UNSUPPORTED;
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return FP4DIT_E_UNSUPPORTED;
+    if (rows < 0 || cols < 0 || cols % head_dim != 0) return FP4DIT_E_SHAPE;
+    if (n_norm_cols < 0 || n_norm_cols > cols || n_norm_cols % head_dim != 0) return FP4DIT_E_SHAPE;
+    if (rows == 0 || cols == 0) return FP4DIT_OK;
+    if (rows * (cols / 8) >= (int64_t(1) << 32)) return FP4DIT_E_SHAPE;
+    if (!x || !out || (n_norm_cols > 0 && !norm_w)) return FP4DIT_E_NULL;
+    if (!aligned(x, 16) || !aligned(out, 16) || (norm_w && !aligned(norm_w, 16))) return FP4DIT_E_ALIGN;
+    return launched(fp4dit::launch_rmsnorm_head(x, rows, cols, head_dim, n_norm_cols, norm_w, eps, out, stream));
+}
+
+fp4dit_status fp4dit_swiglu(const uint16_t* c, int64_t rows, int64_t n_phys, int32_t group, uint16_t* h,
+                            hipStream_t stream) {
+    if (group <= 0 || group % 8 != 0) return FP4DIT_E_UNSUPPORTED;
+    if (rows < 0 || n_phys < 0 || n_phys % (2 * int64_t(group)) != 0) return FP4DIT_E_SHAPE;
+    if (rows == 0 || n_phys == 0) return FP4DIT_OK;
+    if (rows * (n_phys / 16) >= (int64_t(1) << 32)) return FP4DIT_E_SHAPE;
+    if (!c || !h) return FP4DIT_E_NULL;
+    const uintptr_t c0 = reinterpret_cast<uintptr_t>(c), h0 = reinterpret_cast<uintptr_t>(h);
+    if (h0 < c0 + uintptr_t(rows * n_phys * 2) && c0 < h0 + uintptr_t(rows * n_phys)) return FP4DIT_E_UNSUPPORTED;
+    if (!aligned(c, 16) || !aligned(h, 16)) return FP4DIT_E_ALIGN;
+    return launched(fp4dit::launch_swiglu(c, rows, n_phys, group, h, stream));
+}
+
 }  // extern "C"

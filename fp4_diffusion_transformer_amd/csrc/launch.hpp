@@ -39,6 +39,12 @@ hipError_t launch_gemm_swiglu_transform(int64_t M, int64_t N, int64_t K, const u
                                         void* out, bool out_bf16, uint8_t* out_codes, uint8_t* out_scales,
                                         hipStream_t stream);
 
+hipError_t launch_rmsnorm_head(const uint16_t* x, int64_t rows, int64_t cols, int head_dim, int64_t n_norm,
+                               const float* w, float eps, uint16_t* y, hipStream_t stream);
+
+hipError_t launch_swiglu(const uint16_t* c, int64_t rows, int64_t n_phys, int group, uint16_t* h,
+                         hipStream_t stream);
+
 // Interleave group of the SwiGLU epilogue: channel blocks of 32 alternate
 // gate / up, matching one 32x32 MFMA output block per half.
 constexpr int kSwigluGroup = 32;

@@ -54,6 +54,8 @@ def lib():
             "fp4dit_gemm_fp4_epilogue_rmsnorm_head": [I64, I64, I64, P, P, P, P, I32, I64, P, F, P, I32, P],
             "fp4dit_gemm_fp4_epilogue_swiglu": [I64, I64, I64, P, P, P, P, P, I32, P, P, P],
             "fp4dit_gemm_fp4_epilogue_swiglu_transform": [I64, I64, I64, P, P, P, P, P, I64, P, I32, P, P, P],
+            "fp4dit_rmsnorm_head": [P, I64, I64, I32, I64, P, F, P, P],
+            "fp4dit_swiglu": [P, I64, I64, I32, P, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -262,3 +264,32 @@ def gemm_fp4_epilogue_swiglu_transform(a: MxTensor, b: MxTensor, t, y_dtype=None
           _ptr(b.scales), _ptr(t), t.shape[0], _ptr(y), _dtype_code(y.dtype) if y is not None else F32,
           _ptr(mx.codes), _ptr(mx.scales), _stream())
     return y, mx
+
+
+def rmsnorm_head(x, head_dim, n_norm_cols, norm_w, eps=1e-6, out=None):
+    """Unfused per-head RMSNorm of a bf16 [rows, cols] tensor (bf16 result)."""
+    _dev(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bfloat16")
+    if norm_w is not None:
+        _dev(norm_w, "norm_w")
+        if norm_w.dtype != torch.float32:
+            raise ValueError("norm_w must be float32")
+    rows, cols = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _call("fp4dit_rmsnorm_head", _ptr(x), rows, cols, int(head_dim), int(n_norm_cols), _ptr(norm_w), float(eps),
+          _ptr(out), _stream())
+    return out
+
+
+def swiglu(c, group, out=None):
+    """Unfused SwiGLU of a bf16 [rows, n_phys] interleaved GEMM output -> bf16 [rows, n_phys/2]."""
+    _dev(c, "c")
+    if c.dtype != torch.bfloat16:
+        raise ValueError("c must be bfloat16")
+    rows, n_phys = c.shape
+    if out is None:
+        out = torch.empty((rows, n_phys // 2), dtype=torch.bfloat16, device=c.device)
+    _call("fp4dit_swiglu", _ptr(c), rows, n_phys, int(group), _ptr(out), _stream())
+    return out

@@ -263,6 +263,35 @@ fp4dit_status fp4dit_gemm_fp4_epilogue_swiglu_transform(int64_t M, int64_t N, in
                                                         uint8_t* out_codes, uint8_t* out_scales,
                                                         hipStream_t stream);
 
+/*
+ * Unfused epilogues.  fal, "Epilogue fusion in brief": without fusion the
+ * GEMM's output makes a round trip through HBM and each small op is a launch
+ * of its own.  These two calls are those launches, on a bf16 GEMM output
+ * (fp4dit_gemm_fp4_epilogue_none with out_dtype BF16); they exist to measure
+ * what the fused epilogues save, and compute the same definitions on the
+ * bf16 values, in fp32, with a bf16 (round to nearest even) result.
+ *
+ * Per-head RMSNorm, as fp4dit_gemm_fp4_epilogue_rmsnorm_head: x and out
+ * [rows][cols] bf16 bit patterns (out may equal x), 16-byte aligned;
+ * head_dim 128 or 256 with cols % head_dim == 0; n_norm_cols % head_dim
+ * == 0 and <= cols; norm_w [n_norm_cols] float32, 16-byte aligned (may be
+ * NULL only if n_norm_cols == 0); eps >= 0 and finite; rows * cols / 8
+ * below 2^32.
+ */
+fp4dit_status fp4dit_rmsnorm_head(const uint16_t* x, int64_t rows, int64_t cols, int32_t head_dim,
+                                  int64_t n_norm_cols, const float* norm_w, float eps, uint16_t* out,
+                                  hipStream_t stream);
+
+/*
+ * SwiGLU, as fp4dit_gemm_fp4_epilogue_swiglu, over c [rows][n_phys] bf16
+ * whose columns are interleaved with group g (fp4dit_pack_weight's
+ * interleave_group): h [rows][n_phys/2] bf16 = silu(gate) * up.  g % 8 == 0,
+ * n_phys % (2g) == 0, rows * n_phys / 16 below 2^32; c and h 16-byte
+ * aligned and not overlapping (else FP4DIT_E_UNSUPPORTED).
+ */
+fp4dit_status fp4dit_swiglu(const uint16_t* c, int64_t rows, int64_t n_phys, int32_t group, uint16_t* h,
+                            hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

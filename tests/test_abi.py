@@ -37,7 +37,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     raw = ctypes.CDLL(ops.library_path())
     for n in names:
         assert hasattr(raw, n), n
@@ -111,6 +111,25 @@ def test_swiglu_transform_validation(L):
     assert s(*args, P, 1, P, 9, P, P, None) == E_UNSUP
     assert s(256, 320, 512, P, P, P, P, P, 1, None, F32, P, P, None) == E_SHAPE   # N % 256
     assert s(0, 512, 512, None, None, None, None, None, 1, None, F32, None, None, None) == OK
+
+
+def test_unfused_validation(L):
+    r = L.fp4dit_rmsnorm_head
+    assert r(P, 4, 512, 64, 512, P, 1e-6, P, None) == E_UNSUP                # head_dim
+    assert r(P, 4, 384, 256, 256, P, 1e-6, P, None) == E_SHAPE               # cols % head_dim
+    assert r(P, 4, 512, 128, 640, P, 1e-6, P, None) == E_SHAPE               # n_norm > cols
+    assert r(P, 4, 512, 128, 384, None, 1e-6, P, None) == E_NULL
+    assert r(P, 4, 512, 128, 0, None, 1e-6, None, None) == E_NULL            # no output
+    assert r(P + 8, 4, 512, 128, 384, P, 1e-6, P, None) == E_ALIGN
+    assert r(P, 4, 512, 128, 384, P, float("inf"), P, None) == E_UNSUP
+    assert r(None, 0, 512, 128, 384, None, 1e-6, None, None) == OK           # empty
+    sw = L.fp4dit_swiglu
+    assert sw(P, 4, 512, 12, P + 4096, None) == E_UNSUP                       # group % 8
+    assert sw(P, 4, 96, 32, P + 4096, None) == E_SHAPE                        # n_phys % 2g
+    assert sw(P, 4, 512, 32, P + 1024, None) == E_UNSUP                       # h overlaps c
+    assert sw(P, 4, 512, 32, P + 4104, None) == E_ALIGN
+    assert sw(None, 4, 512, 32, P, None) == E_NULL
+    assert sw(None, 0, 512, 32, None, None) == OK
 
 
 def test_transform_pack_fold_validation(L):
