@@ -19,6 +19,9 @@ product.  Sources:
 * sns.style summary of KroQuant (P3): sections "Background and overview"
   (invertible transform on activations, inverse on weights) and "Deep
   analysis" (32-element block-local learned transform, MXFP4 W4A4).
+* fal, QAD section: fake quantisation with a straight-through gradient.
+* "拡散サンプリングの高速化：数値計算手法とスコアベースモデルの出会い" (P4):
+  the ETD1 / ETD2 updates and the Richardson combine.
 
 Modules:
   mxfp4      e2m1 table, e8m0 scales, block quantise / dequantise
@@ -26,10 +29,13 @@ Modules:
              RMSNorm, SwiGLU with column interleave, MXFP4 re-quantisation)
   transform  32-element block-local transform and its weight-side fold
   bf16       round-to-nearest-even float64 -> bfloat16 for output compares
+  qad        MXFP4 fake quantisation (forward) and its straight-through
+             gradient (backward)
+  sampler    ETD1 / ETD2 sampler updates and the Richardson combine
 
 Every function is pinned by a CPU test (tests/test_oracle_*.py) against
 something other than itself: the hand-written code table, exact Fraction
 brute force, closed forms and invariants.
 """
 
-from . import bf16, gemm, mxfp4, transform  # noqa: F401
+from . import bf16, gemm, mxfp4, qad, sampler, transform  # noqa: F401

@@ -12,8 +12,10 @@ import pytest
 import golden_io
 import test_oracle_gemm as tg
 import test_oracle_mxfp4 as tm
+import test_oracle_qad as tq
+import test_oracle_sampler as ts
 import test_oracle_transform as tt
-from oracle import bf16, gemm, mxfp4, transform
+from oracle import bf16, gemm, mxfp4, qad, sampler, transform
 
 
 def _pins_mxfp4():
@@ -47,6 +49,24 @@ def _pins_fused():
         tg.test_swiglu_transform_identity_is_requant(n_t)
     tg.test_swiglu_transform_signed_permutation()
     tg.test_swiglu_transform_keeps_h_unrounded()
+
+
+def _pins_qad():
+    for blk in tq.BLOCKS:
+        if blk[2] != 255:
+            tq.test_fake_quantize_hand_worked_blocks(blk)
+    tq.test_fake_quantize_is_idempotent_and_odd()
+    tq.test_fake_quantize_keeps_grid_values()
+    tq.test_ste_passes_the_gradient_unchanged()
+
+
+def _pins_sampler():
+    for args in [(0.9, 0.7), (0.3, 0.05)]:
+        ts.test_etd1_coefficients_match_the_exact_integral(*args)
+    ts.test_etd1_is_exact_over_many_steps_for_a_constant_prediction()
+    ts.test_etd2_equal_predictions_and_first_step_reduce_to_etd1()
+    for p in (1, 2):
+        ts.test_richardson_cancels_the_leading_error(p)
 
 
 def _pins_transform():
@@ -194,6 +214,33 @@ def _fused_transform_transposed(c_gate, c_up, t, return_scaled=False):
     return mxfp4.quantize(transform.block_transform(gemm.swiglu(c_gate, c_up), t), return_scaled=return_scaled)
 
 
+def _fq_truncating(x):
+    x = np.asarray(x, dtype=np.float64)
+    codes, scales = mxfp4.quantize(x)
+    q = np.abs(x) / np.repeat(mxfp4.e8m0_value(scales), 32, axis=1)
+    grid = mxfp4.E2M1_MAGNITUDES
+    mag = grid[np.clip(np.searchsorted(grid, q, side="right") - 1, 0, 7)]    # round toward zero
+    return np.copysign(mag, x) * np.repeat(mxfp4.e8m0_value(scales), 32, axis=1)
+
+
+def _ste_halved(g):
+    return 0.5 * np.asarray(g, dtype=np.float64)
+
+
+def _etd1_sign_as_printed(alpha_s, sigma_s, alpha_t, sigma_t):
+    h = sampler.log_snr(alpha_t, sigma_t) - sampler.log_snr(alpha_s, sigma_s)
+    return np.exp(h) * alpha_t / alpha_s, alpha_t * (1.0 - np.exp(h))
+
+
+def _etd2_trapezoid(alpha_s, sigma_s, alpha_t, sigma_t, first_step):
+    decay, coeff = sampler.etd1_coefficients(alpha_s, sigma_s, alpha_t, sigma_t)
+    return (decay, coeff, 0.0) if first_step else (decay, 0.5 * coeff, 0.5 * coeff)
+
+
+def _richardson_wrong_denominator(fine, coarse, scale):
+    return (scale * np.asarray(fine, dtype=np.float64) - np.asarray(coarse, dtype=np.float64)) / scale
+
+
 MUTANTS = [
     ("ties_round_up", mxfp4, "encode_magnitude", _ties_up, _pins_mxfp4),
     ("ties_round_down", mxfp4, "encode_magnitude", _ties_down, _pins_mxfp4),
@@ -217,6 +264,11 @@ MUTANTS = [
     ("fused_transform_on_gate", gemm, "swiglu_transform_requantize", _fused_transform_on_gate, _pins_fused),
     ("fused_transform_transposed", gemm, "swiglu_transform_requantize", _fused_transform_transposed,
      _pins_fused),
+    ("fake_quant_truncates", qad, "fake_quantize", _fq_truncating, _pins_qad),
+    ("ste_scales_gradient", qad, "ste_backward", _ste_halved, _pins_qad),
+    ("etd1_exponent_sign_as_printed", sampler, "etd1_coefficients", _etd1_sign_as_printed, _pins_sampler),
+    ("etd2_equal_weights", sampler, "etd2_coefficients", _etd2_trapezoid, _pins_sampler),
+    ("richardson_divides_by_scale", sampler, "richardson_combine", _richardson_wrong_denominator, _pins_sampler),
 ]
 
 
@@ -232,3 +284,5 @@ def test_pins_pass_unmutated():
     _pins_gemm()
     _pins_transform()
     _pins_fused()
+    _pins_qad()
+    _pins_sampler()
