@@ -40,6 +40,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_MXFP4_TFLOPS = 10100.0     # MI355X dense MXFP4 matrix peak
 PEAK_HBM_GBS = 8000.0
 QUANT_BATCH = 20               # back-to-back launches timed for the quantisation figure
+HBM_ROTATE_BYTES = 512 << 20   # buffer sets rotated by an HBM-bound timing touch more than 2x the LLC
+LATENT_SHAPE = (16, 16, 128, 128)   # sampler updates: 16 latents of a 1024x1024 image (16 ch, 8x down)
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -279,6 +281,61 @@ def cpu_baseline(args, layers_wl, rows=2048):
                 rows, ", ".join(w.name for w in layers_wl), elapsed)}
 
 
+def time_rotating(torch, launches, n=QUANT_BATCH):
+    """Average ms of one launch over n back-to-back launches cycling through
+    `launches` (closures over distinct buffer sets)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for f in launches:                                   # untimed pass
+        f()
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n):
+        launches[i % len(launches)]()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def n_sets(bytes_per_set):
+    return max(2, -(-HBM_ROTATE_BYTES // bytes_per_set))
+
+
+def hbm_record(kernel, nbytes, ms, what):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "avg_launch_ms": round(ms, 5), "algorithmic_bytes": nbytes,
+            "measured": what}
+
+
+def aux_kernels(torch, ops, workloads):
+    """The next-row kernels, each HBM-bound, timed on rotating buffer sets:
+    QAD fake quantisation of a DiT-1K activation and the three sampler updates
+    on a batch of latents (fp32)."""
+    out = []
+    wl = workloads.ffn_up_swiglu()
+    x = torch.from_numpy(wl.x).to("cuda", torch.bfloat16)
+    nb = x.numel() * 4                                   # bf16 in, bf16 out
+    sets = [(x.clone(), torch.empty_like(x)) for _ in range(n_sets(nb))]
+    ms = time_rotating(torch, [lambda a=a, b=b: ops.fake_quantize_mxfp4(a, out=b) for a, b in sets])
+    out.append(hbm_record("fake_quantize_mxfp4 (QAD forward, %dx%d bf16 -> bf16)" % tuple(x.shape), nb, ms,
+                          "%d launches over %d buffer sets" % (QUANT_BATCH, len(sets))))
+    del sets
+    n = int(np.prod(LATENT_SHAPE))
+    g = torch.Generator(device="cuda").manual_seed(0)
+    d, c0, c1 = ops.etd_coefficients(0.8, 0.6, 0.9, 0.43589, order=2)
+    for name, n_in, fn in (
+            ("etd1_update", 2, lambda t: ops.etd1_update(t[0], t[1], d, c0 + c1, out=t[-1])),
+            ("etd2_update", 3, lambda t: ops.etd2_update(t[0], t[1], t[2], d, c0, c1, out=t[-1])),
+            ("richardson_combine", 2, lambda t: ops.richardson_combine(t[0], t[1], 4.0, out=t[-1]))):
+        nb = (n_in + 1) * n * 4
+        sets = [[torch.randn(n, device="cuda", generator=g) for _ in range(n_in + 1)] for _ in range(n_sets(nb))]
+        ms = time_rotating(torch, [lambda t=t: fn(t) for t in sets])
+        out.append(hbm_record("%s (%d latents %s fp32)" % (name, LATENT_SHAPE[0], "x".join(map(str, LATENT_SHAPE[1:]))),
+                              nb, ms, "%d launches over %d buffer sets" % (QUANT_BATCH, len(sets))))
+        del sets
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -345,16 +402,15 @@ def main():
     g_avg = float(np.mean(g_ms))
     # The activation-quantisation kernel is ~10 us: a pair of events around a
     # single launch would mostly time the dispatch gap, so after the timed
-    # region it is timed over QUANT_BATCH back-to-back launches instead.
+    # region it is timed over QUANT_BATCH back-to-back launches instead, on
+    # enough input copies that no launch reads what the last-level cache holds.
     Lq = layers[quant_dom]
-    q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    q0.record()
-    for s in range(QUANT_BATCH):
-        Lq.quantize(s)
-    q1.record()
-    torch.cuda.synchronize()
-    q_avg = q0.elapsed_time(q1) / QUANT_BATCH
+    q_sets = [Lq.xs[0].clone() for _ in range(n_sets(Lq.quant_bytes()))]
+    saved = Lq.xs
+    Lq.xs = q_sets
+    q_avg = time_rotating(torch, [lambda i=i: Lq.quantize(i) for i in range(len(q_sets))])
+    Lq.xs = saved
+    del q_sets
     Ld = layers[dom]
     achieved = Ld.flops / (g_avg * 1e-3) / 1e12
     # kernel instantiation as rocprof names it: epilogue, bf16 output, LDS ring
@@ -408,9 +464,11 @@ def main():
             "unit": "GB/s",
             "frac": round(Lq.quant_bytes() / (q_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "avg_launch_ms": round(q_avg, 5),
-            "measured": "events around %d back-to-back launches after the timed region" % QUANT_BATCH,
+            "measured": "events around %d back-to-back launches after the timed region, over %d input copies"
+                        % (QUANT_BATCH, n_sets(Lq.quant_bytes())),
             "algorithmic_bytes": Lq.quant_bytes(),
         },
+        "aux_kernels": aux_kernels(torch, ops, workloads),
     }
     if any(L.unfused for L in layers):
         # each layer's separate epilogue launches, timed like the quantiser

@@ -15,6 +15,13 @@ using fp4dit::kGemmNMultiple;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 bool valid_dtype(fp4dit_dtype d) { return d == FP4DIT_F32 || d == FP4DIT_BF16; }
+bool valid_sampler_dtype(fp4dit_dtype d) { return d == FP4DIT_F32 || d == FP4DIT_BF16 || d == FP4DIT_F16; }
+int dtype_bytes(fp4dit_dtype d) { return d == FP4DIT_F32 ? 4 : 2; }
+// out may be one of the inputs (same start), or else must not overlap it.
+bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x != y && x < y + uintptr_t(b_bytes) && y < x + uintptr_t(a_bytes);
+}
 bool valid_layout(fp4dit_layout l) { return l == FP4DIT_MX_ROWMAJOR || l == FP4DIT_MX_TILED; }
 fp4dit_status launched(hipError_t e) { return e == hipSuccess ? FP4DIT_OK : FP4DIT_E_LAUNCH; }
 
@@ -204,6 +211,86 @@ fp4dit_status fp4dit_swiglu(const uint16_t* c, int64_t rows, int64_t n_phys, int
     if (h0 < c0 + uintptr_t(rows * n_phys * 2) && c0 < h0 + uintptr_t(rows * n_phys)) return FP4DIT_E_UNSUPPORTED;
     if (!aligned(c, 16) || !aligned(h, 16)) return FP4DIT_E_ALIGN;
     return launched(fp4dit::launch_swiglu(c, rows, n_phys, group, h, stream));
+}
+
+fp4dit_status fp4dit_fake_quantize_mxfp4(const void* x, fp4dit_dtype x_dtype, int64_t rows, int64_t cols,
+                                         void* y, fp4dit_dtype y_dtype, hipStream_t stream) {
+    if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return FP4DIT_E_UNSUPPORTED;
+    if (rows < 0 || cols < 0 || cols % 32 != 0) return FP4DIT_E_SHAPE;
+    if (rows == 0 || cols == 0) return FP4DIT_OK;
+    if (rows * (cols / 8) >= (int64_t(1) << 40)) return FP4DIT_E_SHAPE;
+    if (!x || !y) return FP4DIT_E_NULL;
+    if (x == y && x_dtype != y_dtype) return FP4DIT_E_UNSUPPORTED;
+    if (overlaps(x, rows * cols * dtype_bytes(x_dtype), y, rows * cols * dtype_bytes(y_dtype)))
+        return FP4DIT_E_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(y, 16)) return FP4DIT_E_ALIGN;
+    return launched(fp4dit::launch_fake_quant(x, x_dtype == FP4DIT_BF16, rows, cols, y, y_dtype == FP4DIT_BF16,
+                                              stream));
+}
+
+namespace {
+fp4dit_status check_sampler(const void* const* in, int n_in, int64_t n, fp4dit_dtype dtype, const void* out) {
+    if (!valid_sampler_dtype(dtype)) return FP4DIT_E_UNSUPPORTED;
+    if (n < 0 || n >= (int64_t(1) << 40)) return FP4DIT_E_SHAPE;
+    if (n == 0) return FP4DIT_OK;
+    if (!out) return FP4DIT_E_NULL;
+    for (int i = 0; i < n_in; ++i)
+        if (!in[i]) return FP4DIT_E_NULL;
+    for (int i = 0; i < n_in; ++i)
+        if (overlaps(in[i], n * dtype_bytes(dtype), out, n * dtype_bytes(dtype))) return FP4DIT_E_UNSUPPORTED;
+    if (!aligned(out, 16)) return FP4DIT_E_ALIGN;
+    for (int i = 0; i < n_in; ++i)
+        if (!aligned(in[i], 16)) return FP4DIT_E_ALIGN;
+    return FP4DIT_OK;
+}
+}  // namespace
+
+fp4dit_status fp4dit_etd1_update(const void* x, const void* x0, int64_t n, fp4dit_dtype dtype, float decay,
+                                 float coeff, void* out, hipStream_t stream) {
+    const void* in[2] = {x, x0};
+    const fp4dit_status st = check_sampler(in, 2, n, dtype, out);
+    if (st != FP4DIT_OK || n == 0) return st;
+    return launched(fp4dit::launch_etd1(x, x0, n, (int)dtype, decay, coeff, out, stream));
+}
+
+fp4dit_status fp4dit_etd2_update(const void* x, const void* x0, const void* x0_prev, int64_t n,
+                                 fp4dit_dtype dtype, float decay, float c0, float c1, void* out,
+                                 hipStream_t stream) {
+    const void* in[3] = {x, x0, x0_prev};
+    const fp4dit_status st = check_sampler(in, 3, n, dtype, out);
+    if (st != FP4DIT_OK || n == 0) return st;
+    return launched(fp4dit::launch_etd2(x, x0, x0_prev, n, (int)dtype, decay, c0, c1, out, stream));
+}
+
+fp4dit_status fp4dit_richardson_combine(const void* fine, const void* coarse, int64_t n, fp4dit_dtype dtype,
+                                        float scale, void* out, hipStream_t stream) {
+    if (!(scale != 1.0f) || !std::isfinite(scale)) return FP4DIT_E_UNSUPPORTED;
+    const void* in[2] = {fine, coarse};
+    const fp4dit_status st = check_sampler(in, 2, n, dtype, out);
+    if (st != FP4DIT_OK || n == 0) return st;
+    return launched(fp4dit::launch_richardson(fine, coarse, n, (int)dtype, scale, out, stream));
+}
+
+fp4dit_status fp4dit_etd_coefficients(double alpha_s, double sigma_s, double alpha_t, double sigma_t,
+                                      int32_t order, int32_t first_step, double* decay, double* c0,
+                                      double* c1) {
+    if (order != 1 && order != 2) return FP4DIT_E_UNSUPPORTED;
+    const double v[4] = {alpha_s, sigma_s, alpha_t, sigma_t};
+    for (double a : v)
+        if (!(a > 0.0) || !std::isfinite(a)) return FP4DIT_E_SHAPE;
+    if (!decay || !c0 || !c1) return FP4DIT_E_NULL;
+    const double h = std::log(alpha_t / sigma_t) - std::log(alpha_s / sigma_s);
+    const double e = std::exp(-h);
+    const double coeff = alpha_t * (1.0 - e);
+    *decay = e * alpha_t / alpha_s;
+    if (order == 1 || first_step) {
+        *c0 = coeff;
+        *c1 = 0.0;
+    } else {
+        *c0 = 0.75 * coeff;
+        *c1 = 0.25 * coeff;
+    }
+    return FP4DIT_OK;
 }
 
 }  // extern "C"

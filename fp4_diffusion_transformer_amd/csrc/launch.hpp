@@ -45,6 +45,17 @@ hipError_t launch_rmsnorm_head(const uint16_t* x, int64_t rows, int64_t cols, in
 hipError_t launch_swiglu(const uint16_t* c, int64_t rows, int64_t n_phys, int group, uint16_t* h,
                          hipStream_t stream);
 
+hipError_t launch_fake_quant(const void* x, bool x_bf16, int64_t rows, int64_t cols, void* y, bool y_bf16,
+                             hipStream_t stream);
+
+// Sampler updates; storage: 0 fp32, 1 bf16, 2 fp16 (the fp4dit_dtype values).
+hipError_t launch_etd1(const void* x, const void* x0, int64_t n, int storage, float decay, float coeff, void* out,
+                       hipStream_t stream);
+hipError_t launch_etd2(const void* x, const void* x0, const void* x0_prev, int64_t n, int storage, float decay,
+                       float c0, float c1, void* out, hipStream_t stream);
+hipError_t launch_richardson(const void* fine, const void* coarse, int64_t n, int storage, float scale, void* out,
+                             hipStream_t stream);
+
 // Interleave group of the SwiGLU epilogue: channel blocks of 32 alternate
 // gate / up, matching one 32x32 MFMA output block per half.
 constexpr int kSwigluGroup = 32;

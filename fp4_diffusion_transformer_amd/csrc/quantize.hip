@@ -81,6 +81,72 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
     }
 }
 
+// QAD fake quantisation (fal, QAD section: the forward pass goes through the
+// FP4 rounding, the backward pass passes the gradient straight through, so
+// it needs no kernel): y = D(Q(x)), blocks of 32 along the row, the same
+// unit layout and encoding as quantize_kernel, then each code decoded back.
+// The decoded values (e2m1 level times a power of two, at most two
+// significant bits) are exact in fp32 and in bf16, including the subnormal
+// ones (fp32 denormals are kept), so the bf16 result is the fp32 one with its
+// low 16 bits, which are zero, dropped.  A block holding Inf / NaN gives NaN.
+template <bool kBf16In, bool kBf16Out>
+__global__ __launch_bounds__(256) void fake_quant_kernel(const void* __restrict__ x, void* __restrict__ y,
+                                                         int64_t nunits) {
+    const int64_t unit = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (unit >= nunits) return;                  // whole quads leave together (nunits % 4 == 0)
+    const int64_t elem = unit * 8;
+    uint32_t xb[8];
+    if (kBf16In) {
+        const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(static_cast<const uint16_t*>(x) + elem));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            xb[2 * j] = v[j] << 16;
+            xb[2 * j + 1] = v[j] & 0xFFFF0000u;
+        }
+    } else {
+        const v4u* p = reinterpret_cast<const v4u*>(static_cast<const float*>(x) + elem);
+        const v4u v0 = __builtin_nontemporal_load(p), v1 = __builtin_nontemporal_load(p + 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            xb[j] = v0[j];
+            xb[4 + j] = v1[j];
+        }
+    }
+    uint32_t amax = 0u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t a = xb[j] & 0x7FFFFFFFu;
+        amax = a > amax ? a : amax;
+    }
+    const uint32_t sc = e8m0_from_amax_bits(max_quad_u(amax));
+    float xf[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xf[j] = __uint_as_float(xb[j]);
+    const uint32_t enc = e2m1_pack8(xf, sc);
+    // level * 2 of magnitude codes 0..7 (0, 1, 2, 3, 4, 6, 8, 12), one nibble each
+    constexpr uint32_t kTwiceLevel = 0xC8643210u;
+    // 2^(shared - 1) = 2^(sc - 128): a normal fp32 for sc >= 2, else 2^-127 / 2^-128
+    const uint32_t p2 = sc >= 2u ? (sc - 1u) << 23 : 0x00400000u >> (1u - sc);
+    const float half_scale = __uint_as_float(p2);
+    uint32_t yb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t c = (enc >> (4 * j)) & 15u;
+        const float mag = (float)((kTwiceLevel >> (4 * (c & 7u))) & 15u) * half_scale;
+        yb[j] = sc == 0xFFu ? 0x7FC00000u : (__float_as_uint(mag) | ((c & 8u) << 28));
+    }
+    if (kBf16Out) {
+        v4u v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = (yb[2 * j] >> 16) | (yb[2 * j + 1] & 0xFFFF0000u);
+        __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(static_cast<uint16_t*>(y) + elem));
+    } else {
+        v4u* p = reinterpret_cast<v4u*>(static_cast<float*>(y) + elem);
+        __builtin_nontemporal_store((v4u){yb[0], yb[1], yb[2], yb[3]}, p);
+        __builtin_nontemporal_store((v4u){yb[4], yb[5], yb[6], yb[7]}, p + 1);
+    }
+}
+
 // One thread per output block (physical column p, K-block kb): gathers the 32
 // weights of logical column src(p), rows 32kb..32kb+31, and encodes them.
 template <bool kBf16, bool kTiled>
@@ -154,6 +220,20 @@ hipError_t launch_pack_weight(const void* w, bool bf16, int64_t K, int64_t N, in
         if (tiled) FP4DIT_P(false, true); else FP4DIT_P(false, false);
     }
 #undef FP4DIT_P
+    return hipGetLastError();
+}
+
+hipError_t launch_fake_quant(const void* x, bool x_bf16, int64_t rows, int64_t cols, void* y, bool y_bf16,
+                             hipStream_t stream) {
+    const int64_t nunits = rows * (cols / 8);
+    const dim3 grid((unsigned)((nunits + 255) / 256));
+#define FP4DIT_FQ(A, B) hipLaunchKernelGGL((fake_quant_kernel<A, B>), grid, dim3(256), 0, stream, x, y, nunits)
+    if (x_bf16) {
+        if (y_bf16) FP4DIT_FQ(true, true); else FP4DIT_FQ(true, false);
+    } else {
+        if (y_bf16) FP4DIT_FQ(false, true); else FP4DIT_FQ(false, false);
+    }
+#undef FP4DIT_FQ
     return hipGetLastError();
 }
 

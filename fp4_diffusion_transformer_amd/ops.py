@@ -16,6 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 
 F32 = 0
 BF16 = 1
+F16 = 2
 ROWMAJOR = 0
 TILED = 1
 _LAYOUTS = {"rowmajor": ROWMAJOR, "tiled": TILED}
@@ -56,11 +57,18 @@ def lib():
             "fp4dit_gemm_fp4_epilogue_swiglu_transform": [I64, I64, I64, P, P, P, P, P, I64, P, I32, P, P, P],
             "fp4dit_rmsnorm_head": [P, I64, I64, I32, I64, P, F, P, P],
             "fp4dit_swiglu": [P, I64, I64, I32, P, P],
+            "fp4dit_fake_quantize_mxfp4": [P, I32, I64, I64, P, I32, P],
+            "fp4dit_etd1_update": [P, P, I64, I32, F, F, P, P],
+            "fp4dit_etd2_update": [P, P, P, I64, I32, F, F, F, P, P],
+            "fp4dit_richardson_combine": [P, P, I64, I32, F, P, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
+        D, PD = ctypes.c_double, ctypes.POINTER(ctypes.c_double)
+        L.fp4dit_etd_coefficients.argtypes = [D, D, D, D, I32, I32, PD, PD, PD]
+        L.fp4dit_etd_coefficients.restype = ctypes.c_int
         L.fp4dit_swiglu_interleave_group.argtypes = []
         L.fp4dit_swiglu_interleave_group.restype = ctypes.c_int32
         L.fp4dit_status_string.argtypes = [ctypes.c_int]
@@ -91,12 +99,14 @@ def _dev(t, name):
     return t
 
 
-def _dtype_code(dt):
+def _dtype_code(dt, allow_f16=False):
     if dt == torch.float32:
         return F32
     if dt == torch.bfloat16:
         return BF16
-    raise ValueError("dtype must be float32 or bfloat16, got %s" % dt)
+    if allow_f16 and dt == torch.float16:
+        return F16
+    raise ValueError("dtype must be float32 or bfloat16%s, got %s" % (" or float16" if allow_f16 else "", dt))
 
 
 def swiglu_interleave_group():
@@ -293,3 +303,80 @@ def swiglu(c, group, out=None):
         out = torch.empty((rows, n_phys // 2), dtype=torch.bfloat16, device=c.device)
     _call("fp4dit_swiglu", _ptr(c), rows, n_phys, int(group), _ptr(out), _stream())
     return out
+
+
+# ------------------------------------------------------------------- QAD --
+def fake_quantize_mxfp4(x, y_dtype=None, out=None):
+    """y = D(Q(x)) per 32-element block of each row (float32 / bfloat16)."""
+    _dev(x, "x")
+    rows, cols = x.shape
+    if out is None:
+        out = torch.empty((rows, cols), dtype=y_dtype or x.dtype, device=x.device)
+    _call("fp4dit_fake_quantize_mxfp4", _ptr(x), _dtype_code(x.dtype), rows, cols, _ptr(out),
+          _dtype_code(out.dtype), _stream())
+    return out
+
+
+class _FakeQuantSTE(torch.autograd.Function):
+    """Forward: the fake-quantisation kernel.  Backward: the straight-through
+    estimator hands the incoming gradient on unchanged."""
+
+    @staticmethod
+    def forward(ctx, x):
+        return fake_quantize_mxfp4(x.contiguous())
+
+    @staticmethod
+    def backward(ctx, grad_y):
+        return grad_y
+
+
+def fake_quantize_ste(x):
+    return _FakeQuantSTE.apply(x)
+
+
+# --------------------------------------------------------------- sampler --
+def _same(ts, names):
+    for t, nm in zip(ts, names):
+        _dev(t, nm)
+        if t.dtype != ts[0].dtype or t.numel() != ts[0].numel():
+            raise ValueError("%s must match %s in dtype and size" % (nm, names[0]))
+    return _dtype_code(ts[0].dtype, allow_f16=True), ts[0].numel()
+
+
+def etd1_update(x, x0, decay, coeff, out=None):
+    """out = decay * x + coeff * x0 (elementwise, fp32 arithmetic)."""
+    code, n = _same([x, x0], ["x", "x0"])
+    if out is None:
+        out = torch.empty_like(x)
+    _same([x, out], ["x", "out"])
+    _call("fp4dit_etd1_update", _ptr(x), _ptr(x0), n, code, float(decay), float(coeff), _ptr(out), _stream())
+    return out
+
+
+def etd2_update(x, x0, x0_prev, decay, c0, c1, out=None):
+    """out = decay * x + c0 * x0 + c1 * x0_prev."""
+    code, n = _same([x, x0, x0_prev], ["x", "x0", "x0_prev"])
+    if out is None:
+        out = torch.empty_like(x)
+    _same([x, out], ["x", "out"])
+    _call("fp4dit_etd2_update", _ptr(x), _ptr(x0), _ptr(x0_prev), n, code, float(decay), float(c0), float(c1),
+          _ptr(out), _stream())
+    return out
+
+
+def richardson_combine(fine, coarse, scale, out=None):
+    """out = (scale * fine - coarse) / (scale - 1); scale = 2^p."""
+    code, n = _same([fine, coarse], ["fine", "coarse"])
+    if out is None:
+        out = torch.empty_like(fine)
+    _same([fine, out], ["fine", "out"])
+    _call("fp4dit_richardson_combine", _ptr(fine), _ptr(coarse), n, code, float(scale), _ptr(out), _stream())
+    return out
+
+
+def etd_coefficients(alpha_s, sigma_s, alpha_t, sigma_t, order=1, first_step=False):
+    """(decay, c0, c1) of one ETD step (host arithmetic in the library)."""
+    d, c0, c1 = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _call("fp4dit_etd_coefficients", float(alpha_s), float(sigma_s), float(alpha_t), float(sigma_t), int(order),
+          int(bool(first_step)), ctypes.byref(d), ctypes.byref(c0), ctypes.byref(c1))
+    return d.value, c0.value, c1.value

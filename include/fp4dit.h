@@ -72,7 +72,8 @@ typedef enum fp4dit_status {
 
 typedef enum fp4dit_dtype {
     FP4DIT_F32 = 0,           /* IEEE binary32                                  */
-    FP4DIT_BF16 = 1           /* bfloat16 (uint16 bit patterns)                 */
+    FP4DIT_BF16 = 1,          /* bfloat16 (uint16 bit patterns)                 */
+    FP4DIT_F16 = 2            /* IEEE binary16 (sampler updates only)           */
 } fp4dit_dtype;
 
 typedef enum fp4dit_layout {
@@ -291,6 +292,59 @@ fp4dit_status fp4dit_rmsnorm_head(const uint16_t* x, int64_t rows, int64_t cols,
  */
 fp4dit_status fp4dit_swiglu(const uint16_t* c, int64_t rows, int64_t n_phys, int32_t group, uint16_t* h,
                             hipStream_t stream);
+
+/*
+ * QAD fake quantisation (fal, QAD section: the student's forward pass goes
+ * through its own FP4 rounding, so the quantisation noise propagates; the
+ * backward pass routes the gradient around the rounding with a
+ * straight-through estimator, i.e. dL/dx = dL/dy, which needs no kernel).
+ * y = D(Q(x)): every 32-element block of a row is quantised exactly as
+ * fp4dit_quantize_mxfp4 does and each code is replaced by its value,
+ * level * 2^s.  Those values are exact in F32 and in BF16, so the result is
+ * unique (bit-exact, -0 for code 0x8); a block holding Inf or NaN gives NaN.
+ * x [rows][cols] of x_dtype, y [rows][cols] of y_dtype (F32 or BF16 each),
+ * both 16-byte aligned; y may equal x when the dtypes match; cols % 32 == 0.
+ */
+fp4dit_status fp4dit_fake_quantize_mxfp4(const void* x, fp4dit_dtype x_dtype, int64_t rows, int64_t cols,
+                                         void* y, fp4dit_dtype y_dtype, hipStream_t stream);
+
+/*
+ * Diffusion-sampler updates ("拡散サンプリングの高速化：数値計算手法と
+ * スコアベースモデルの出会い", sections on the exponential integrator, on
+ * Richardson extrapolation and on the fused update kernels), elementwise over
+ * n elements of one dtype (F32, BF16 or F16; every pointer 16-byte aligned;
+ * out may equal an input but not overlap one otherwise), computed in fp32
+ * and rounded once (to nearest even) into the dtype:
+ *   ETD1        out = decay * x + coeff * x0
+ *   ETD2        out = decay * x + c0 * x0 + c1 * x0_prev
+ *   Richardson  out = (scale * fine - coarse) / (scale - 1), scale != 1
+ * x is the current state, x0 / x0_prev the network's data predictions at
+ * this step and the previous one, fine / coarse the results of an order-p
+ * method with 2N and N steps (scale = 2^p).  n < 2^40.
+ */
+fp4dit_status fp4dit_etd1_update(const void* x, const void* x0, int64_t n, fp4dit_dtype dtype, float decay,
+                                 float coeff, void* out, hipStream_t stream);
+fp4dit_status fp4dit_etd2_update(const void* x, const void* x0, const void* x0_prev, int64_t n,
+                                 fp4dit_dtype dtype, float decay, float c0, float c1, void* out,
+                                 hipStream_t stream);
+fp4dit_status fp4dit_richardson_combine(const void* fine, const void* coarse, int64_t n, fp4dit_dtype dtype,
+                                        float scale, void* out, hipStream_t stream);
+
+/*
+ * Host-only: the scalars of one ETD step from schedule point (alpha_s,
+ * sigma_s) to (alpha_t, sigma_t), all > 0, with h = lambda_t - lambda_s and
+ * lambda = log(alpha / sigma) (same page, exponential-integrator section):
+ *   decay = e^-h * alpha_t / alpha_s,  coeff = alpha_t * (1 - e^-h),
+ * the coefficients that make the step exact for a data prediction held
+ * constant over it.  order 1 (ETD1): c0 = coeff, c1 = 0.  order 2 (ETD2):
+ * c0 = 3/4 coeff, c1 = 1/4 coeff, except on the first step (first_step != 0),
+ * which has no previous prediction and is ETD1.  Computed in double.
+ * Returns FP4DIT_E_UNSUPPORTED for another order, FP4DIT_E_SHAPE for a
+ * non-positive or non-finite schedule value, FP4DIT_E_NULL for a NULL output.
+ */
+fp4dit_status fp4dit_etd_coefficients(double alpha_s, double sigma_s, double alpha_t, double sigma_t,
+                                      int32_t order, int32_t first_step, double* decay, double* c0,
+                                      double* c1);
 
 #ifdef __cplusplus
 }

@@ -37,7 +37,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 17
     raw = ctypes.CDLL(ops.library_path())
     for n in names:
         assert hasattr(raw, n), n
@@ -130,6 +130,59 @@ def test_unfused_validation(L):
     assert sw(P, 4, 512, 32, P + 4104, None) == E_ALIGN
     assert sw(None, 4, 512, 32, P, None) == E_NULL
     assert sw(None, 0, 512, 32, None, None) == OK
+
+
+def test_fake_quant_validation(L):
+    f = L.fp4dit_fake_quantize_mxfp4
+    assert f(P, BF16, 4, 48, P + 4096, BF16, None) == E_SHAPE                 # cols % 32
+    assert f(P, 2, 4, 64, P + 4096, BF16, None) == E_UNSUP                    # F16 is for the sampler only
+    assert f(P, BF16, 4, 64, P, F32, None) == E_UNSUP                         # in place across dtypes
+    assert f(P, F32, 4, 64, P + 512, BF16, None) == E_UNSUP                   # overlap (x spans 1 KiB)
+    assert f(P, BF16, 4, 64, P + 4104, BF16, None) == E_ALIGN
+    assert f(None, BF16, 4, 64, P, BF16, None) == E_NULL
+    assert f(None, BF16, 0, 64, None, BF16, None) == OK
+
+
+def test_sampler_validation(L):
+    F16 = 2
+    e1, e2, rc = L.fp4dit_etd1_update, L.fp4dit_etd2_update, L.fp4dit_richardson_combine
+    assert e1(P, P + 4096, 100, 7, 0.5, 0.5, P + 8192, None) == E_UNSUP       # dtype
+    assert e1(P, P + 4096, -1, F16, 0.5, 0.5, P + 8192, None) == E_SHAPE
+    assert e1(P, None, 100, F16, 0.5, 0.5, P + 8192, None) == E_NULL
+    assert e1(P, P + 4096, 100, F32, 0.5, 0.5, P + 200, None) == E_UNSUP     # out overlaps x
+    # out == x passes the overlap check (the misaligned x0 is what fails)
+    assert e1(P, P + 4100, 100, F32, 0.5, 0.5, P, None) == E_ALIGN
+    assert e1(P + 4, P + 4096, 100, F32, 0.5, 0.5, P + 8192, None) == E_ALIGN
+    assert e2(P, P + 4096, None, 100, BF16, 0.5, 0.3, 0.1, P + 8192, None) == E_NULL
+    assert rc(P, P + 4096, 100, F32, 1.0, P + 8192, None) == E_UNSUP          # scale 1
+    assert rc(None, None, 0, F32, 2.0, None, None) == OK
+
+
+def test_etd_coefficients_host_logic(L):
+    """The host helper against the oracle's coefficients (no GPU involved)."""
+    import math
+    from oracle import sampler
+
+    def vp(t):
+        a = math.cos(0.5 * math.pi * t)
+        return a, math.sqrt(1.0 - a * a)
+
+    d, c0, c1 = (ctypes.c_double() for _ in range(3))
+    for s, t in [(0.9, 0.8), (0.5, 0.3), (0.2, 0.05)]:
+        args = (*vp(s), *vp(t))
+        for order, first in [(1, 0), (2, 1), (2, 0)]:
+            assert L.fp4dit_etd_coefficients(*args, order, first, ctypes.byref(d), ctypes.byref(c0),
+                                             ctypes.byref(c1)) == OK
+            if order == 1:
+                ref = sampler.etd1_coefficients(*args) + (0.0,)
+            else:
+                ref = sampler.etd2_coefficients(*args, first_step=bool(first))
+            assert (d.value, c0.value, c1.value) == pytest.approx(ref, rel=1e-14, abs=1e-300)
+    assert L.fp4dit_etd_coefficients(0.5, 0.5, 0.6, 0.4, 3, 0, ctypes.byref(d), ctypes.byref(c0),
+                                     ctypes.byref(c1)) == E_UNSUP
+    assert L.fp4dit_etd_coefficients(0.5, 0.0, 0.6, 0.4, 1, 0, ctypes.byref(d), ctypes.byref(c0),
+                                     ctypes.byref(c1)) == E_SHAPE
+    assert L.fp4dit_etd_coefficients(0.5, 0.5, 0.6, 0.4, 1, 0, None, ctypes.byref(c0), ctypes.byref(c1)) == E_NULL
 
 
 def test_transform_pack_fold_validation(L):
