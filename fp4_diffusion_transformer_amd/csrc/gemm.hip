@@ -491,12 +491,17 @@ __device__ __forceinline__ void transform_block(float* hv, const v8s (&tf)[2]) {
 // 256-wide head (both channel halves) are exchanged through its last 2 KiB.
 // acc[nb][mb][i]: channel n0 + wn*128 + nb*32 + 8*(i/4) + 4h + i%4,
 //                 token   m0 + wm*128 + mb*32 + r32.
-// after_mb(mb) runs once the outputs of token block mb are stored (it issues
-// the next tile's prefetch in pieces, so that the stores are not queued
-// behind all of it).
-template <int EPI, bool OUT_BF16, typename AfterMb>
+// The next tile's prefetch is issued through the two hooks:
+// * plain / RMSNorm: early() runs once this tile's own loads (the norm
+//   gains) are issued and before any store, so that every store comes after
+//   the prefetch in the in-order VMEM counter and the next tile's first
+//   barrier can leave the stores in flight (tile_start_barrier);
+// * SwiGLU: after_mb(mb) runs once token block mb is stored (all 256
+//   accumulators live at the start leave no registers for the load offsets
+//   there; the requant's stores are few).
+template <int EPI, bool OUT_BF16, typename Early, typename AfterMb>
 __device__ __forceinline__ void epilogue(v16f (&acc)[4][4], const GemmArgs& g, int64_t n0, int64_t m0,
-                                         uint8_t* stg, int wave, AfterMb after_mb) {
+                                         uint8_t* stg, int wave, Early early, AfterMb after_mb) {
     const int lane = fresh_lane_id();
     const int wn = wave & 1, wm = wave >> 1;
     const int r32 = lane & 31, h = lane >> 5;
@@ -505,7 +510,28 @@ __device__ __forceinline__ void epilogue(v16f (&acc)[4][4], const GemmArgs& g, i
     uint8_t* region = stg + wave * kStageOutBytes;
     if (EPI == kEpiNone || EPI == kEpiRmsNorm) {
         float rstd[4] = {1.f, 1.f, 1.f, 1.f};
-        bool norm = false;
+        const int64_t head0 = g.head_dim == 256 ? n0 : cbase;
+        const bool norm = EPI == kEpiRmsNorm && head0 < g.n_norm;
+        // gains through a buffer descriptor sized to n_norm: the loads are
+        // unconditional (no branches, so the compiler's VMEM counting stays
+        // exact and nothing waits for the prefetch), columns past n_norm read 0
+        v4f wv[4][4];
+        if (EPI == kEpiRmsNorm) {
+            const __amdgpu_buffer_rsrc_t wr =
+                buffer_rsrc(reinterpret_cast<const uint8_t*>(g.norm_w), g.norm_w ? g.n_norm * 4 : 0);
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const v4u w = __builtin_amdgcn_raw_buffer_load_b128(
+                        wr, (int)(cbase + nb * 32 + 8 * a + 4 * h) * 4, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) wv[nb][a][r] = norm ? __uint_as_float(w[r]) : 1.f;
+                }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        early();
+        __builtin_amdgcn_sched_barrier(0);
         if (EPI == kEpiRmsNorm) {
             float* red = reinterpret_cast<float*>(stg + kRedOff);   // [2 wn][256 tokens]
             float ss[4];
@@ -528,21 +554,12 @@ __device__ __forceinline__ void epilogue(v16f (&acc)[4][4], const GemmArgs& g, i
                 for (int mb = 0; mb < 4; ++mb) ss[mb] += red[(1 - wn) * kBM + wm * 128 + mb * 32 + r32];
                 ring_barrier<63>();                       // red overlaps the rows staged next
             }
-            const int64_t head0 = g.head_dim == 256 ? n0 : cbase;
-            norm = head0 < g.n_norm;
-            const float inv_d = 1.0f / (float)g.head_dim;
+            // head_dim is 128 or 256: a constant select (an SGPR), not a division whose
+            // result would be kept live in a VGPR across the main loop
+            const float inv_d = g.head_dim == 256 ? 1.0f / 256.0f : 1.0f / 128.0f;
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) rstd[mb] = rsqrtf(ss[mb] * inv_d + g.eps);
         }
-        v4f wv[4][4];
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                wv[nb][a] = (v4f){1.f, 1.f, 1.f, 1.f};
-                if (EPI == kEpiRmsNorm && norm)
-                    wv[nb][a] = *reinterpret_cast<const v4f*>(g.norm_w + cbase + nb * 32 + 8 * a + 4 * h);
-            }
         auto vals = [&](int q, int mb, float* v) {
             const int nb = q >> 2, a = q & 3;
 #pragma unroll
@@ -567,7 +584,6 @@ __device__ __forceinline__ void epilogue(v16f (&acc)[4][4], const GemmArgs& g, i
                     }
                 }
             }
-            after_mb(mb);
         }
     }
 
@@ -652,6 +668,18 @@ __device__ __forceinline__ void epilogue(v16f (&acc)[4][4], const GemmArgs& g, i
     }
 }
 
+// First barrier of a tile after a full-tile plain / RMSNorm epilogue: wait
+// for the first prefetched stage only.  VMEM operations issued after it:
+// the other prefetched stages (VM0 loads), then the epilogue's stores, 8
+// (bf16 rows staged through LDS) or 16 (fp32 rows) per token block; every
+// store of a full tile is issued, so VM0 + stores (capped at the counter's
+// 63) is at most what follows stage 0.
+template <bool OUT_BF16, int VM0>
+__device__ __forceinline__ void tile_start_barrier() {
+    constexpr int kStores = 4 * (OUT_BF16 ? 8 : 16);
+    ring_barrier<(VM0 + kStores < 63 ? VM0 + kStores : 63)>();
+}
+
 // Persistent kernel: workgroup b runs tiles b, b + G, b + 2G, ... (G = grid
 // size, a multiple of 8 so every tile of one workgroup maps to its own XCD).
 // The first NS - 1 K stages of the next tile load while the current tile's
@@ -693,6 +721,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
     const int n_issue = kt_count - D;
 
     int v = blockIdx.x;
+    bool relaxed = false;
     int tm, tn;
     tile_of(v, n_tiles, tiles_n, tiles_m, tm, tn);
     {
@@ -713,7 +742,10 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = (v16f){};
 
-        ring_barrier<kVmPrologue>();                   // stage 0 landed
+        if (relaxed)                                   // stage 0 landed; stores may still drain
+            tile_start_barrier<OUT_BF16, kVmPrologue>();
+        else
+            ring_barrier<kVmPrologue>();
         Frags f0, f1;
         uint32_t wsc[4], xsc[4];
         read_scales(wsc, xsc, slots[OFF % NS], wn, wm, r32, h);
@@ -748,12 +780,23 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
         // finish this tile; after its token block j (< D) is stored, stage j
         // of the next tile starts loading (its load offsets are formed there
         // rather than kept live through the epilogue)
-        epilogue<EPI, OUT_BF16>(acc, g, n0, m0, stg, wave, [&](int mb) {
-            if (more && mb < D)
-                issue_stage_at(slots[(mb + OFF) % NS], ops, make_plan(M, K, tn * kBN, tm * kBM, wave, fresh_lane_id()),
-                               mb, wave);
-        });
+        constexpr bool kEarly = EPI == kEpiNone || EPI == kEpiRmsNorm;
+        epilogue<EPI, OUT_BF16>(
+            acc, g, n0, m0, stg, wave,
+            [&]() {
+                if (kEarly && more) {
+                    const LoadPlan pl = make_plan(M, K, tn * kBN, tm * kBM, wave, fresh_lane_id());
+                    static_for<0, D>([&](auto j) { issue_stage_at(slots[(j() + OFF) % NS], ops, pl, j(), wave); });
+                }
+            },
+            [&](int mb) {
+                if (!kEarly && more && mb < D)
+                    issue_stage_at(slots[(mb + OFF) % NS], ops,
+                                   make_plan(M, K, tn * kBN, tm * kBM, wave, fresh_lane_id()), mb, wave);
+            });
         if (!more) break;
+        // after a full tile every store of the epilogue followed the prefetch
+        relaxed = kEarly && m0 + kBM <= M;
         v = vn;
     }
 }
