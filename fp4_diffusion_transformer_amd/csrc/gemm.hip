@@ -499,17 +499,21 @@ __device__ __forceinline__ void transform_block(float* hv, const v8s (&tf)[2]) {
 // * SwiGLU: after_mb(mb) runs once token block mb is stored (all 256
 //   accumulators live at the start leave no registers for the load offsets
 //   there; the requant's stores are few).
-template <int EPI, bool OUT_BF16, typename Early, typename AfterMb>
-__device__ __forceinline__ void epilogue(v16f (&acc)[4][4], const GemmArgs& g, int64_t n0, int64_t m0,
+// MB: token blocks of 32 per wave (4 for a full 256-token tile, 1 for a
+// quarter tile of 64 tokens).
+template <int EPI, bool OUT_BF16, int MB, typename Early, typename AfterMb>
+__device__ __forceinline__ void epilogue(v16f (&acc)[4][MB], const GemmArgs& g, int64_t n0, int64_t m0,
                                          uint8_t* stg, int wave, Early early, AfterMb after_mb) {
     const int lane = fresh_lane_id();
     const int wn = wave & 1, wm = wave >> 1;
     const int r32 = lane & 31, h = lane >> 5;
     const int64_t cbase = n0 + wn * 128;
-    const int64_t tok0 = m0 + wm * 128;
+    const int64_t tok0 = m0 + wm * (32 * MB);
     uint8_t* region = stg + wave * kStageOutBytes;
     if (EPI == kEpiNone || EPI == kEpiRmsNorm) {
-        float rstd[4] = {1.f, 1.f, 1.f, 1.f};
+        float rstd[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) rstd[mb] = 1.f;
         const int64_t head0 = g.head_dim == 256 ? n0 : cbase;
         const bool norm = EPI == kEpiRmsNorm && head0 < g.n_norm;
         // gains through a buffer descriptor sized to n_norm: the loads are
@@ -534,9 +538,9 @@ __device__ __forceinline__ void epilogue(v16f (&acc)[4][4], const GemmArgs& g, i
         __builtin_amdgcn_sched_barrier(0);
         if (EPI == kEpiRmsNorm) {
             float* red = reinterpret_cast<float*>(stg + kRedOff);   // [2 wn][256 tokens]
-            float ss[4];
+            float ss[MB];
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
+            for (int mb = 0; mb < MB; ++mb) {
                 float s = 0.f;
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb)
@@ -547,18 +551,18 @@ __device__ __forceinline__ void epilogue(v16f (&acc)[4][4], const GemmArgs& g, i
             if (g.head_dim == 256) {                      // head = both channel halves
                 if (h == 0) {
 #pragma unroll
-                    for (int mb = 0; mb < 4; ++mb) red[wn * kBM + wm * 128 + mb * 32 + r32] = ss[mb];
+                    for (int mb = 0; mb < MB; ++mb) red[wn * kBM + wm * (32 * MB) + mb * 32 + r32] = ss[mb];
                 }
                 ring_barrier<63>();                       // LDS only: the prefetch stays in flight
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb) ss[mb] += red[(1 - wn) * kBM + wm * 128 + mb * 32 + r32];
+                for (int mb = 0; mb < MB; ++mb) ss[mb] += red[(1 - wn) * kBM + wm * (32 * MB) + mb * 32 + r32];
                 ring_barrier<63>();                       // red overlaps the rows staged next
             }
             // head_dim is 128 or 256: a constant select (an SGPR), not a division whose
             // result would be kept live in a VGPR across the main loop
             const float inv_d = g.head_dim == 256 ? 1.0f / 256.0f : 1.0f / 128.0f;
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) rstd[mb] = rsqrtf(ss[mb] * inv_d + g.eps);
+            for (int mb = 0; mb < MB; ++mb) rstd[mb] = rsqrtf(ss[mb] * inv_d + g.eps);
         }
         auto vals = [&](int q, int mb, float* v) {
             const int nb = q >> 2, a = q & 3;
@@ -568,7 +572,7 @@ __device__ __forceinline__ void epilogue(v16f (&acc)[4][4], const GemmArgs& g, i
                                                     : acc[nb][mb][4 * a + r];
         };
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
             if (OUT_BF16) {
                 store_bf16_half<16>(region, [&](int q, float* v) { vals(q, mb, v); }, static_cast<uint16_t*>(g.out),
                                     g.N, tok0 + mb * 32, cbase, g.M, r32, h, lane);
@@ -596,7 +600,7 @@ __device__ __forceinline__ void epilogue(v16f (&acc)[4][4], const GemmArgs& g, i
         v8s tf[2][2];
         if (EPI == kEpiSwigluTransform) load_t_frags(tf, g, ob0 / 32, r32, h);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
             float hv[2][16];                  // [p][4a + r]
 #pragma unroll
             for (int p = 0; p < 2; ++p)
@@ -680,6 +684,114 @@ __device__ __forceinline__ void tile_start_barrier() {
     ring_barrier<(VM0 + kStores < 63 ? VM0 + kStores : 63)>();
 }
 
+// ------------------------------------------------------------ quarter tiles
+// When the 256 x 256 tiles leave a partial last round (576 tiles on 256 CUs
+// are 2.25 rounds), the tiles of that round are split into quarter tiles of
+// 256 channels x 64 tokens, as many as there are workgroups for each of
+// them: waves (wn, wm) own 128 channels x 32 tokens (acc[4][1]).  The four
+// quarters of a tile run on one XCD, so its weight rows come into one L2.
+// Per stage a wave loads 4 weight-code chunks of 16 rows (as in the full
+// tile), 16 token rows, its 64 weight-scale rows and, on 16 lanes, its 16
+// token-scale rows: kQDma loads.  The K loop is compiler-scheduled: it runs
+// once per workgroup at the end, where the full tiles' schedule would leave
+// three quarters of the CUs idle.
+constexpr int kQDma = 7;
+
+struct QPlan {
+    uint32_t w_code[4], x_code, w_scale, x_scale;
+};
+
+__device__ __forceinline__ QPlan make_qplan(int M, int K, int n0, int m0, int wave, int lane) {
+    QPlan p;
+    const uint32_t kq = (uint32_t)(K / 128);
+    const int rin = lane >> 2;
+    const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        p.w_code[j] = code_tile_off((uint32_t)(n0 + (wave * 4 + j) * 16 + rin), kq) + lchunk * 16;
+    const int xr = m0 + wave * 16 + rin < M ? m0 + wave * 16 + rin : M - 1;
+    p.x_code = code_tile_off((uint32_t)xr, kq) + lchunk * 16;
+    p.w_scale = scale_tile_off((uint32_t)(n0 + wave * 64 + lane), kq);
+    const int sr = m0 + wave * 16 + (lane & 15) < M ? m0 + wave * 16 + (lane & 15) : M - 1;
+    p.x_scale = scale_tile_off((uint32_t)sr, kq);
+    return p;
+}
+
+__device__ __forceinline__ void issue_qstage(uint8_t* stage, const Operands& o, const QPlan& p, int kt, int wave,
+                                             int lane) {
+    const uint32_t soff = (uint32_t)kt * 128u;
+    const uint32_t base = opaque_sgpr(lds_addr(stage));
+    auto lds = [](uint32_t a) { return (lds_void*)(uintptr_t)a; };
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(o.wc, lds(base + kWCodesOff + (wave * 4 + j) * 1024), 16, p.w_code[j],
+                                                 soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(o.xc, lds(base + kXCodesOff + wave * 1024), 16, p.x_code, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(o.ws, lds(base + kWScalesOff + wave * 256), 4, p.w_scale, soff, 0, 0);
+    if (lane < 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(o.xs, lds(base + kXScalesOff + wave * 64), 4, p.x_scale, soff, 0, 0);
+}
+
+// One K stage of a quarter tile on ring slot `cur`: 2 K-steps x 4 MFMAs.
+__device__ __forceinline__ void q_stage(v16f (&acc)[4][1], const uint8_t* cur_, int wn, int wm, int r32, int h) {
+    uint32_t zero = 0;
+    asm volatile("" : "+s"(zero));
+    const uint8_t* cur = cur_ + zero;
+    uint32_t wsc[4], xsc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        wsc[i] = *reinterpret_cast<const uint16_t*>(cur + kWScalesOff + (wn * 128 + i * 32 + r32) * kScaleBytes + 2 * h);
+    xsc = *reinterpret_cast<const uint16_t*>(cur + kXScalesOff + (wm * 32 + r32) * kScaleBytes + 2 * h);
+    v4i w[2][4], x[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        const int chunk = ((2 * h + st) ^ ((r32 >> 2) & 3)) * 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[st][i] = *reinterpret_cast<const v4i*>(cur + kWCodesOff + (wn * 128 + i * 32 + r32) * kRowBytes + chunk);
+        x[st] = *reinterpret_cast<const v4i*>(cur + kXCodesOff + (wm * 32 + r32) * kRowBytes + chunk);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mfma_one<0>(acc[i][0], w[0][i], x[0], wsc[i], xsc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mfma_one<1>(acc[i][0], w[1][i], x[1], wsc[i], xsc);
+}
+
+// Quarter tile (n0, m0: its 256 channels and 64 tokens): prologue of D
+// stages, the K loop (stage kt in slot (kt + OFF) % NS, so slot indices stay
+// compile-time constants), then the epilogue on a free slot.
+template <int EPI, bool OUT_BF16, int NS, int OFF>
+__device__ __forceinline__ void quarter_tile(const GemmArgs& g, const Operands& ops, uint8_t* const* slots, int n0,
+                                             int m0, int wave) {
+    constexpr int D = NS - 1;
+    const int M = (int)g.M, K = (int)g.K;
+    const int kt_count = K / kBK;
+    const int wn = wave & 1, wm = wave >> 1;
+    const int lane = fresh_lane_id();
+    const int r32 = lane & 31, h = lane >> 5;
+    const QPlan plan = make_qplan(M, K, n0, m0, wave, lane);
+    static_for<0, D>([&](auto j) { issue_qstage(slots[(j() + OFF) % NS], ops, plan, j(), wave, lane); });
+    v16f acc[4][1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i][0] = (v16f){};
+    for (int kt0 = 0; kt0 < kt_count; kt0 += NS) {
+        static_for<0, NS>([&](auto sidx) {
+            constexpr int kS = decltype(sidx)::value;
+            const int kt = kt0 + kS;
+            if (kt < kt_count) {
+                // stage kt landed (only stage kt + 1's loads may remain), and
+                // every wave is done with the slot stage kt + D refills
+                if (kt + 1 < kt_count) ring_barrier<(D - 1) * kQDma>();
+                else ring_barrier<0>();
+                if (kt + D < kt_count) issue_qstage(slots[(kS + D + OFF) % NS], ops, plan, kt + D, wave, lane);
+                q_stage(acc, slots[(kS + OFF) % NS], wn, wm, r32, h);
+            }
+        });
+    }
+    ring_barrier<63>();                                // every wave is done reading the ring
+    epilogue<EPI, OUT_BF16, 1>(acc, g, n0, m0, slots[(OFF + D) % NS], wave, [] {}, [](int) {});
+}
+
 // Persistent kernel: workgroup b runs tiles b, b + G, b + 2G, ... (G = grid
 // size, a multiple of 8 so every tile of one workgroup maps to its own XCD).
 // The first NS - 1 K stages of the next tile load while the current tile's
@@ -719,6 +831,19 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
     uint8_t* const slots[4] = {ring0, ring1, ring2, ring3};
     uint8_t* const stg = slots[(OFF + D) % NS];
     const int n_issue = kt_count - D;
+    constexpr bool kEarly = EPI == kEpiNone || EPI == kEpiRmsNorm;
+
+    // A partial last round of full tiles runs as quarter tiles instead (plain
+    // and RMSNorm epilogues; the round's tile count a multiple of the 8 XCDs):
+    // virtual tiles [0, n_full) are full, [n_full, n_virtual) quarters.
+    int n_full = n_tiles, n_virtual = n_tiles;
+    if constexpr (kEarly) {
+        const int G = (int)gridDim.x, rem = n_tiles % G;
+        if (rem != 0 && (rem & 7) == 0 && (G & 7) == 0) {
+            n_full = n_tiles - rem;
+            n_virtual = n_full + 4 * rem;
+        }
+    }
 
     int v = blockIdx.x;
     bool relaxed = false;
@@ -775,13 +900,12 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
         ring_barrier<63>();                            // every wave is done reading the ring
 
         const int vn = v + (int)gridDim.x;
-        const bool more = vn < n_tiles;
+        const bool more = vn < n_full;                 // the next tile is a full one
         if (more) tile_of(vn, n_tiles, tiles_n, tiles_m, tm, tn);
-        // finish this tile; after its token block j (< D) is stored, stage j
-        // of the next tile starts loading (its load offsets are formed there
-        // rather than kept live through the epilogue)
-        constexpr bool kEarly = EPI == kEpiNone || EPI == kEpiRmsNorm;
-        epilogue<EPI, OUT_BF16>(
+        // finish this tile; the next full tile's first stages load meanwhile
+        // (their load offsets are formed there rather than kept live through
+        // the epilogue)
+        epilogue<EPI, OUT_BF16, 4>(
             acc, g, n0, m0, stg, wave,
             [&]() {
                 if (kEarly && more) {
@@ -794,10 +918,24 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
                     issue_stage_at(slots[(mb + OFF) % NS], ops,
                                    make_plan(M, K, tn * kBN, tm * kBM, wave, fresh_lane_id()), mb, wave);
             });
-        if (!more) break;
+        if (!more) {
+            if constexpr (kEarly) v = vn;              // on to the quarter tiles
+            break;
+        }
         // after a full tile every store of the epilogue followed the prefetch
         relaxed = kEarly && m0 + kBM <= M;
         v = vn;
+    }
+    // quarter tiles: q = v - n_full -> XCD q % 8, quarter (q / 8) % 4 of the
+    // partial round's tile n_full + (q / 32) * 8 + q % 8 (workgroup ids, and
+    // so q, are congruent to their XCD mod 8: a tile's quarters share one)
+    if constexpr (kEarly) {
+        for (; v < n_virtual; v += (int)gridDim.x) {
+            const int q = v - n_full;
+            int ptm, ptn;
+            tile_of(n_full + ((q >> 5) << 3) + (q & 7), n_tiles, tiles_n, tiles_m, ptm, ptn);
+            quarter_tile<EPI, OUT_BF16, NS, OFF>(g, ops, slots, ptn * kBN, ptm * kBM + ((q >> 3) & 3) * 64, wave);
+        }
     }
 }
 

@@ -170,11 +170,13 @@ def test_swiglu_requant(with_bf16):
     assert exc_codes <= 0.001 * h_ref.size
 
 
-@pytest.mark.parametrize("epilogue", ["none", "rmsnorm", "swiglu_requant"])
+@pytest.mark.parametrize("epilogue", ["none", "rmsnorm", "rmsnorm256", "swiglu_requant"])
 def test_persistent_many_tiles_ragged(epilogue):
     """More 256 x 256 tiles (4 x 80 = 320) than a persistent grid holds, so
     workgroups run several tiles in turn (the next tile's loads overlapping
-    the epilogue), with a ragged last token tile (1000 = 3 * 256 + 232)."""
+    the epilogue), with a ragged last token tile (1000 = 3 * 256 + 232).  On
+    a 256-CU device the plain and RMSNorm epilogues run the partial second
+    round (64 tiles) as 256 quarter tiles of 64 tokens."""
     rng = np.random.default_rng(31)
     m, n, k = 1000, 256 * 80, 512
     rows = np.unique(np.concatenate([[0, 255, 256, 767, 768, 999], rng.choice(m, 40, replace=False)]))
@@ -193,12 +195,13 @@ def test_persistent_many_tiles_ragged(epilogue):
         out = ops.gemm_fp4_epilogue_none(*_dev_ops(ac, as_, bc, bs), out_dtype=torch.float32)
         parity.assert_close(host(out)[rows], c, parity.TOL_F32, what="persistent none")
     else:
+        hd = 256 if epilogue == "rmsnorm256" else 128
         n_norm = n - 2048
         norm_w = rng.uniform(0.5, 1.5, n_norm).astype(np.float32)
-        ref = ogemm.rmsnorm_head(c, 128, n_norm, norm_w.astype(np.float64), 1e-6)
-        out = ops.gemm_fp4_epilogue_rmsnorm_head(*_dev_ops(ac, as_, bc, bs), 128, n_norm,
+        ref = ogemm.rmsnorm_head(c, hd, n_norm, norm_w.astype(np.float64), 1e-6)
+        out = ops.gemm_fp4_epilogue_rmsnorm_head(*_dev_ops(ac, as_, bc, bs), hd, n_norm,
                                                  dev(norm_w, torch.float32), 1e-6, out_dtype=torch.bfloat16)
-        parity.assert_close(host(out)[rows], ref, parity.TOL_BF16, group=128, what="persistent rmsnorm")
+        parity.assert_close(host(out)[rows], ref, parity.TOL_BF16, group=hd, what="persistent " + epilogue)
 
 
 # SwiGLU -> down-projection block transform -> MXFP4, fused in the epilogue
