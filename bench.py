@@ -415,10 +415,11 @@ def main():
     achieved = Ld.flops / (g_avg * 1e-3) / 1e12
     # kernel instantiation as rocprof names it: epilogue, bf16 output, LDS ring
     # depth (3) and the K stages peeled before its unrolled loop
-    out_bf16 = Ld.out is not None or Ld.unfused
+    # output kind template argument: 0 no `out` (requant only), 1 bf16, 2 fp32
+    out_kind = 1 if (Ld.out is not None or Ld.unfused) else 0
     kt, ring = Ld.k // 128, 3
     epi_name = "none" if Ld.unfused else Ld.wl.epilogue + ("_transform" if Ld.next_t is not None else "")
-    kernel_key = "gemm_%s<%s,%d,%d>" % (epi_name, "true" if out_bf16 else "false", ring, (kt - ring + 1) % ring)
+    kernel_key = "gemm_%s<%d,%d,%d>" % (epi_name, out_kind, ring, (kt - ring + 1) % ring)
 
     out = {
         "metric": "fused MXFP4 GEMM+epilogue TFLOPS and % of MXFP4 peak at DiT 1K shapes",

@@ -29,6 +29,11 @@ fp4dit_status launched(hipError_t e) { return e == hipSuccess ? FP4DIT_OK : FP4D
 // to an even number of rows).
 constexpr int64_t kMaxOperandBytes = (int64_t(1) << 31) - 1;
 
+// The requant epilogue forms its output offsets in 32 bits.
+bool requant_fits(int64_t M, int64_t N) {
+    return (M + 1) * (N / 4) <= kMaxOperandBytes && (M + 31) * (N / 64) <= kMaxOperandBytes;
+}
+
 fp4dit_status check_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
                          const uint8_t* bc, const uint8_t* bs) {
     if (M < 0 || N <= 0 || K <= 0) return FP4DIT_E_SHAPE;
@@ -158,6 +163,7 @@ fp4dit_status fp4dit_gemm_fp4_epilogue_swiglu(int64_t M, int64_t N, int64_t K, c
     const fp4dit_status st = check_gemm(M, N, K, a_codes, a_scales, b_codes, b_scales);
     if (st != FP4DIT_OK) return st;
     if (N % (2 * fp4dit::kSwigluGroup) != 0) return FP4DIT_E_SHAPE;
+    if (out_codes && !requant_fits(M, N)) return FP4DIT_E_SHAPE;
     if (M == 0) return FP4DIT_OK;
     if (!out && !out_codes) return FP4DIT_E_NULL;
     if ((out && !aligned(out, 16)) || (out_codes && (!aligned(out_codes, 16) || !aligned(out_scales, 2))))
@@ -177,6 +183,7 @@ fp4dit_status fp4dit_gemm_fp4_epilogue_swiglu_transform(int64_t M, int64_t N, in
     if (st != FP4DIT_OK) return st;
     if (N % (2 * fp4dit::kSwigluGroup) != 0) return FP4DIT_E_SHAPE;
     if (n_t != 1 && n_t != N / 64) return FP4DIT_E_SHAPE;
+    if (!requant_fits(M, N)) return FP4DIT_E_SHAPE;
     if (M == 0) return FP4DIT_OK;
     if (!t_bf16 || !out_codes || !out_scales) return FP4DIT_E_NULL;
     if ((y && !aligned(y, 16)) || !aligned(t_bf16, 2) || !aligned(out_codes, 16) || !aligned(out_scales, 2))

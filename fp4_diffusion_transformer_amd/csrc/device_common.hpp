@@ -22,21 +22,36 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- e8m0 ----
-// Shared exponent of a block from the bits of its largest magnitude.
-// Returns the e8m0 byte (shared + 127); 0xFF when amax is Inf or NaN, 0 for
-// an all-zero block.  Branch-free (selects only).
+// Shared exponent of a block from the bits of its largest magnitude (sign
+// bit clear).  Returns the e8m0 byte (shared + 127) of shared =
+// clamp(floor(log2 amax) - 2, -127, 127): for a normal amax with exponent
+// field e that is max(e - 2, 0) (e - 129 never exceeds 125); a subnormal
+// amax has floor(log2) - 2 <= -129, clamped to byte 0, and so has zero --
+// the same max(e - 2, 0) with e = 0.  Inf / NaN (e = 255): 0xFF.
 __device__ __forceinline__ uint32_t e8m0_from_amax_bits(uint32_t amax_bits) {
     const uint32_t e = amax_bits >> 23;
-    // floor(log2 amax): from the exponent field, or for a subnormal amax
-    // from the position of its leading one (value = bits * 2^-149)
-    const int normal = (int)e - 127;
-    const int subnormal = (31 - (int)__builtin_clz(amax_bits | 1u)) - 149;
-    const int pick = -(int)(e != 0u);                   // all ones for a normal amax
-    const int floor_log2 = (normal & pick) | (subnormal & ~pick);
-    int shared = floor_log2 - 2;
-    shared = shared < -127 ? -127 : (shared > 127 ? 127 : shared);
-    const uint32_t s = (uint32_t)(shared + 127);
-    return amax_bits >= 0x7F800000u ? 0xFFu : (amax_bits == 0u ? 0u : s);
+    const uint32_t s = e > 2u ? e - 2u : 0u;
+    return e >= 255u ? 0xFFu : s;
+}
+
+// Largest magnitude of n fp32 values, as sign-cleared bits (a NaN ranks
+// above Inf, Inf above every finite value).  Two max chains over the raw
+// bits instead of a mask per value: as signed integers the non-negative
+// floats order by magnitude and beat every negative one; as unsigned
+// integers the negative ones order by magnitude and beat every
+// non-negative one.
+template <int N>
+__device__ __forceinline__ uint32_t amax_bits(const float* v) {
+    int si = (int)__float_as_uint(v[0]);
+    uint32_t su = __float_as_uint(v[0]);
+#pragma unroll
+    for (int i = 1; i < N; ++i) {
+        const uint32_t b = __float_as_uint(v[i]);
+        si = (int)b > si ? (int)b : si;
+        su = b > su ? b : su;
+    }
+    const uint32_t a = (uint32_t)si & 0x7FFFFFFFu, c = su & 0x7FFFFFFFu;
+    return a > c ? a : c;
 }
 
 // --------------------------------------------------------------- e2m1 -----

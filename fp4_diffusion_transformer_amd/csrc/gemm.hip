@@ -70,6 +70,9 @@ constexpr int kDmaPerStage = 10;       // direct-to-LDS instructions per wave pe
 constexpr int kDmaEarly = 8;           // of them issued before the stage's barrier
 
 enum EpiKind { kEpiNone = 0, kEpiRmsNorm = 1, kEpiSwiglu = 2, kEpiSwigluTransform = 3 };
+// What the `out` array receives (a compile-time choice, so a kernel holds
+// only the store code it runs): nothing (SwiGLU requant only), bf16, fp32.
+enum OutKind { kOutNone = 0, kOutBf16 = 1, kOutF32 = 2 };
 
 struct GemmArgs {
     int64_t M, N, K;
@@ -501,7 +504,7 @@ __device__ __forceinline__ void transform_block(float* hv, const v8s (&tf)[2]) {
 //   there; the requant's stores are few).
 // MB: token blocks of 32 per wave (4 for a full 256-token tile, 1 for a
 // quarter tile of 64 tokens).
-template <int EPI, bool OUT_BF16, int MB, typename Early, typename AfterMb>
+template <int EPI, int OUT, int MB, typename Early, typename AfterMb>
 __device__ __forceinline__ void epilogue(v16f (&acc)[4][MB], const GemmArgs& g, int64_t n0, int64_t m0,
                                          uint8_t* stg, int wave, Early early, AfterMb after_mb) {
     const int lane = fresh_lane_id();
@@ -573,7 +576,7 @@ __device__ __forceinline__ void epilogue(v16f (&acc)[4][MB], const GemmArgs& g, 
         };
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            if (OUT_BF16) {
+            if (OUT == kOutBf16) {
                 store_bf16_half<16>(region, [&](int q, float* v) { vals(q, mb, v); }, static_cast<uint16_t*>(g.out),
                                     g.N, tok0 + mb * 32, cbase, g.M, r32, h, lane);
             } else {
@@ -611,8 +614,8 @@ __device__ __forceinline__ void epilogue(v16f (&acc)[4][MB], const GemmArgs& g, 
                 for (int p = 0; p < 2; ++p) transform_block(hv[p], tf[p]);
             }
             const int64_t tok = tok0 + mb * 32 + r32;
-            if (g.out != nullptr) {
-                if (OUT_BF16) {
+            if (OUT != kOutNone) {
+                if (OUT == kOutBf16) {
                     store_bf16_half<8>(region, [&](int q, float* v) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) v[r] = hv[q >> 2][4 * (q & 3) + r];
@@ -629,41 +632,43 @@ __device__ __forceinline__ void epilogue(v16f (&acc)[4][MB], const GemmArgs& g, 
             }
             if (g.out_codes != nullptr) {
                 // Requant of the two 32-output blocks b = ob0/32 + p (p = 0, 1)
-                // of token tok: lane h gathers block b + h whole (16 bytes,
-                // half of its codes from the partner lane l ^ 32) and stores
-                // it with one 16-byte store; lanes h = 0 store both scale
-                // bytes (adjacent in the tiled layout, b even) as one u16.
-                uint32_t sc[2];
-                uint32_t c16[2][4];                   // [p][a]: codes of outputs 8a+4h .. +3
+                // of token tok.  own[p][j]: this lane's codes of block p,
+                // outputs 8a + 4h + r of a = 2j (bytes 0, 1) and a = 2j + 1
+                // (bytes 2, 3).  One lane swap of (own[0][j], own[1][j])
+                // leaves, in every lane, the h = 0 codes (x) and the h = 1
+                // codes (y) of block b + h, so dword a of its 16-byte row is
+                // two byte permutes away; lanes h = 0 store both scale bytes
+                // (adjacent in the tiled layout, b even) as one u16.
+                uint32_t sc[2], own[2][2];
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
-                    uint32_t amax = 0u;
+                    sc[p] = e8m0_from_amax_bits(max_xor32_u(amax_bits<16>(hv[p])));
+                    const float s8 = __uint_as_float(sc[p] << 23);
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const uint32_t a = __float_as_uint(hv[p][i]) & 0x7FFFFFFFu;
-                        amax = a > amax ? a : amax;
-                    }
-                    sc[p] = e8m0_from_amax_bits(max_xor32_u(amax));
-#pragma unroll
-                    for (int a = 0; a < 4; ++a) {
-                        const uint32_t c = e2m1_pack4(&hv[p][4 * a], sc[p]);
-                        c16[p][a] = sc[p] == 0xFFu ? 0u : c;   // Inf / NaN block: zero codes
+                    for (int j = 0; j < 2; ++j) {
+                        uint32_t w = 0u;
+                        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, hv[p][8 * j], hv[p][8 * j + 1], s8, 0);
+                        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, hv[p][8 * j + 2], hv[p][8 * j + 3], s8, 1);
+                        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, hv[p][8 * j + 4], hv[p][8 * j + 5], s8, 2);
+                        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, hv[p][8 * j + 6], hv[p][8 * j + 7], s8, 3);
+                        own[p][j] = sc[p] == 0xFFu ? 0u : w;     // Inf / NaN block: zero codes
                     }
                 }
-                // lane h keeps block h and sends block 1 - h (two dwords)
-                const uint32_t send0 = h == 0 ? (c16[1][0] | (c16[1][1] << 16)) : (c16[0][0] | (c16[0][1] << 16));
-                const uint32_t send1 = h == 0 ? (c16[1][2] | (c16[1][3] << 16)) : (c16[0][2] | (c16[0][3] << 16));
-                const uint32_t recv0 = partner_xor32(send0, lane);
-                const uint32_t recv1 = partner_xor32(send1, lane);
-                const uint32_t rc[4] = {recv0 & 0xFFFFu, recv0 >> 16, recv1 & 0xFFFFu, recv1 >> 16};
                 v4u st;                                // dword a: outputs 8a .. 8a+7 of block b + h
 #pragma unroll
-                for (int a = 0; a < 4; ++a) st[a] = h == 0 ? (c16[0][a] | (rc[a] << 16)) : (rc[a] | (c16[1][a] << 16));
+                for (int j = 0; j < 2; ++j) {
+                    const auto xy = __builtin_amdgcn_permlane32_swap(own[0][j], own[1][j], false, false);
+                    st[2 * j] = __builtin_amdgcn_perm(xy[1], xy[0], 0x05040100u);
+                    st[2 * j + 1] = __builtin_amdgcn_perm(xy[1], xy[0], 0x07060302u);
+                }
                 if (tok < g.M) {                       // MX_TILED output, ready for the next GEMM
-                    const int64_t blk = ob0 / 32;
-                    *reinterpret_cast<v4u*>(g.out_codes + tiled_code_off(tok, (blk + h) * 32, nh)) = st;
+                    // 32-bit offsets: the host keeps both outputs below 2^31 bytes
+                    const uint32_t t = (uint32_t)tok, kt = (uint32_t)nh >> 7, blk = (uint32_t)ob0 >> 5;
+                    const uint32_t coff = (((t >> 1) * kt + ((blk + h) >> 2)) << 7) + ((t & 1) << 6) + ((blk + h) & 3) * 16;
+                    *reinterpret_cast<v4u*>(g.out_codes + coff) = st;
                     if (h == 0)
-                        *reinterpret_cast<uint16_t*>(g.out_scales + tiled_scale_off(tok, blk, nh)) =
+                        *reinterpret_cast<uint16_t*>(g.out_scales + ((((t >> 5) * kt + (blk >> 2)) << 7) +
+                                                                     ((t & 31) << 2) + (blk & 3))) =
                             (uint16_t)(sc[0] | (sc[1] << 8));
                 }
             }
@@ -678,10 +683,25 @@ __device__ __forceinline__ void epilogue(v16f (&acc)[4][MB], const GemmArgs& g, 
 // (bf16 rows staged through LDS) or 16 (fp32 rows) per token block; every
 // store of a full tile is issued, so VM0 + stores (capped at the counter's
 // 63) is at most what follows stage 0.
-template <bool OUT_BF16, int VM0>
+template <int OUT, int VM0>
 __device__ __forceinline__ void tile_start_barrier() {
-    constexpr int kStores = 4 * (OUT_BF16 ? 8 : 16);
+    constexpr int kStores = 4 * (OUT == kOutBf16 ? 8 : 16);
     ring_barrier<(VM0 + kStores < 63 ? VM0 + kStores : 63)>();
+}
+
+// The same after a full-tile SwiGLU epilogue, whose prefetch goes out in two
+// pieces: stage 0 after token block 0's stores, stage 1 after block 1's.
+// After stage 0 come the stores of blocks 1..3 (3 x per_mb) and stage 1's
+// VM0 loads; per_mb = 4 (bf16 h rows) or 8 (fp32) + 2 (code and scale
+// stores), as configured.  Each branch's count is at most that.
+template <int VM0>
+__device__ __forceinline__ void tile_start_barrier_swiglu(int per_mb) {
+    if (per_mb >= 10) ring_barrier<VM0 + 30>();
+    else if (per_mb >= 8) ring_barrier<VM0 + 24>();
+    else if (per_mb >= 6) ring_barrier<VM0 + 18>();
+    else if (per_mb >= 4) ring_barrier<VM0 + 12>();
+    else if (per_mb >= 2) ring_barrier<VM0 + 6>();
+    else ring_barrier<VM0>();
 }
 
 // ------------------------------------------------------------ quarter tiles
@@ -760,7 +780,7 @@ __device__ __forceinline__ void q_stage(v16f (&acc)[4][1], const uint8_t* cur_, 
 // Quarter tile (n0, m0: its 256 channels and 64 tokens): prologue of D
 // stages, the K loop (stage kt in slot (kt + OFF) % NS, so slot indices stay
 // compile-time constants), then the epilogue on a free slot.
-template <int EPI, bool OUT_BF16, int NS, int OFF>
+template <int EPI, int OUT, int NS, int OFF>
 __device__ __forceinline__ void quarter_tile(const GemmArgs& g, const Operands& ops, uint8_t* const* slots, int n0,
                                              int m0, int wave) {
     constexpr int D = NS - 1;
@@ -789,7 +809,7 @@ __device__ __forceinline__ void quarter_tile(const GemmArgs& g, const Operands& 
         });
     }
     ring_barrier<63>();                                // every wave is done reading the ring
-    epilogue<EPI, OUT_BF16, 1>(acc, g, n0, m0, slots[(OFF + D) % NS], wave, [] {}, [](int) {});
+    epilogue<EPI, OUT, 1>(acc, g, n0, m0, slots[(OFF + D) % NS], wave, [] {}, [](int) {});
 }
 
 // Persistent kernel: workgroup b runs tiles b, b + G, b + 2G, ... (G = grid
@@ -798,7 +818,7 @@ __device__ __forceinline__ void quarter_tile(const GemmArgs& g, const Operands& 
 // epilogue runs, one stage after each of its first token blocks is stored.
 // NS: ring depth (kRing); PEEL: (K/128 - NS + 1) % NS, the stages run before
 // the unrolled loop.
-template <int EPI, bool OUT_BF16, int NS, int PEEL>
+template <int EPI, int OUT, int NS, int PEEL>
 __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
     static_assert(NS >= 2 && NS <= kRing && PEEL < NS, "ring shape");
     __shared__ __attribute__((aligned(1024))) uint8_t ring0[kStageBytes];
@@ -867,10 +887,18 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = (v16f){};
 
-        if (relaxed)                                   // stage 0 landed; stores may still drain
-            tile_start_barrier<OUT_BF16, kVmPrologue>();
-        else
+        if (relaxed) {                                 // stage 0 landed; stores may still drain
+            if constexpr (kEarly)
+                tile_start_barrier<OUT, kVmPrologue>();
+            else
+                // (without `out` the requant output is always set)
+                tile_start_barrier_swiglu<kVmPrologue>(
+                    OUT == kOutNone ? 2
+                                    : __builtin_amdgcn_readfirstlane((OUT == kOutBf16 ? 4 : 8) +
+                                                                     (g.out_codes == nullptr ? 0 : 2)));
+        } else {
             ring_barrier<kVmPrologue>();
+        }
         Frags f0, f1;
         uint32_t wsc[4], xsc[4];
         read_scales(wsc, xsc, slots[OFF % NS], wn, wm, r32, h);
@@ -905,7 +933,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
         // finish this tile; the next full tile's first stages load meanwhile
         // (their load offsets are formed there rather than kept live through
         // the epilogue)
-        epilogue<EPI, OUT_BF16, 4>(
+        epilogue<EPI, OUT, 4>(
             acc, g, n0, m0, stg, wave,
             [&]() {
                 if (kEarly && more) {
@@ -922,8 +950,9 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
             if constexpr (kEarly) v = vn;              // on to the quarter tiles
             break;
         }
-        // after a full tile every store of the epilogue followed the prefetch
-        relaxed = kEarly && m0 + kBM <= M;
+        // after a full tile every store of the epilogue was issued (the
+        // plain / RMSNorm ones all after the prefetch)
+        relaxed = __builtin_amdgcn_readfirstlane((int)(m0 + kBM <= M)) != 0;   // uniform: keep it scalar
         v = vn;
     }
     // quarter tiles: q = v - n_full -> XCD q % 8, quarter (q / 8) % 4 of the
@@ -934,34 +963,42 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
             const int q = v - n_full;
             int ptm, ptn;
             tile_of(n_full + ((q >> 5) << 3) + (q & 7), n_tiles, tiles_n, tiles_m, ptm, ptn);
-            quarter_tile<EPI, OUT_BF16, NS, OFF>(g, ops, slots, ptn * kBN, ptm * kBM + ((q >> 3) & 3) * 64, wave);
+            quarter_tile<EPI, OUT, NS, OFF>(g, ops, slots, ptn * kBN, ptm * kBM + ((q >> 3) & 3) * 64, wave);
         }
     }
 }
 
-template <int EPI, bool OUT_BF16, int NS>
+template <int EPI, int OUT, int NS>
 void launch_peel(const GemmArgs& g, int peel, dim3 grid, hipStream_t stream) {
     static_for_host<0, NS>([&](auto p) {
         constexpr int kPeel = decltype(p)::value;
         if (peel == kPeel)
-            hipLaunchKernelGGL((gemm_fp4_kernel<EPI, OUT_BF16, NS, kPeel>), grid, dim3(256), 0, stream, g);
+            hipLaunchKernelGGL((gemm_fp4_kernel<EPI, OUT, NS, kPeel>), grid, dim3(256), 0, stream, g);
     });
 }
 
 // A kRing-deep ring needs at least kRing - 1 K stages: K >= 256 gives two.
-template <int EPI, bool OUT_BF16>
+template <int EPI, int OUT>
 void launch_ring(const GemmArgs& g, dim3 grid, hipStream_t stream) {
     static_assert(kRing - 1 <= kGemmKMultiple / kBK, "ring deeper than the shortest K");
     const int kt_count = (int)(g.K / kBK);
-    launch_peel<EPI, OUT_BF16, kRing>(g, (kt_count - (kRing - 1)) % kRing, grid, stream);
+    launch_peel<EPI, OUT, kRing>(g, (kt_count - (kRing - 1)) % kRing, grid, stream);
 }
 
+// `out` NULL (only the SwiGLU epilogues allow it: their requant output is
+// set then), bf16 or fp32.
 template <int EPI>
 void launch_epi(const GemmArgs& g, bool out_bf16, dim3 grid, hipStream_t stream) {
+    if constexpr (EPI == kEpiSwiglu || EPI == kEpiSwigluTransform) {
+        if (g.out == nullptr) {
+            launch_ring<EPI, kOutNone>(g, grid, stream);
+            return;
+        }
+    }
     if (out_bf16) {
-        launch_ring<EPI, true>(g, grid, stream);
+        launch_ring<EPI, kOutBf16>(g, grid, stream);
     } else {
-        launch_ring<EPI, false>(g, grid, stream);
+        launch_ring<EPI, kOutF32>(g, grid, stream);
     }
 }
 

@@ -28,13 +28,7 @@ typedef short v8s __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ void store_mx_block(const float* hv, int lane, bool live,
                                                uint8_t* codes16, uint8_t* scale1) {
     const int h = lane >> 5;
-    uint32_t amax = 0u;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const uint32_t a = __float_as_uint(hv[i]) & 0x7FFFFFFFu;
-        amax = a > amax ? a : amax;
-    }
-    amax = max_xor32_u(amax);
+    const uint32_t amax = max_xor32_u(amax_bits<16>(hv));
     const uint32_t sc = e8m0_from_amax_bits(amax);
     uint32_t c16[4];
 #pragma unroll

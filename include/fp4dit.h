@@ -227,7 +227,8 @@ fp4dit_status fp4dit_gemm_fp4_epilogue_rmsnorm_head(int64_t M, int64_t N, int64_
  * out_codes, out_scales  both NULL, or both set: MXFP4 re-quantisation of
  *            the fp32 h [M][N/2] along its columns, in the MX_TILED layout
  *            (ready to be the A operand of the next GEMM; codes 16-byte,
- *            scales 2-byte aligned), encoded as fp4dit_quantize_mxfp4 does.
+ *            scales 2-byte aligned), encoded as fp4dit_quantize_mxfp4 does;
+ *            both buffers below 2^31 bytes (else FP4DIT_E_SHAPE).
  * At least one output must be set.
  */
 fp4dit_status fp4dit_gemm_fp4_epilogue_swiglu(int64_t M, int64_t N, int64_t K,
@@ -254,7 +255,8 @@ fp4dit_status fp4dit_gemm_fp4_epilogue_swiglu(int64_t M, int64_t N, int64_t K,
  * out_codes, out_scales  required: MXFP4 codes / scales of y in the
  *            MX_TILED layout (codes 16-byte, scales 2-byte aligned), ready
  *            to be the A operand of the down-projection GEMM, whose weights
- *            carry the inverse transform (fp4dit_fold_inverse_transform).
+ *            carry the inverse transform (fp4dit_fold_inverse_transform);
+ *            both below 2^31 bytes (else FP4DIT_E_SHAPE).
  */
 fp4dit_status fp4dit_gemm_fp4_epilogue_swiglu_transform(int64_t M, int64_t N, int64_t K,
                                                         const uint8_t* a_codes, const uint8_t* a_scales,
