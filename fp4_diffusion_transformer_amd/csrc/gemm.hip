@@ -454,13 +454,18 @@ __device__ __forceinline__ void k_stage(v16f (&acc)[4][4], Frags& f0, Frags& f1,
 // takes bf16, so h is split into hi = bf16(h) and lo = bf16(h - hi) and both
 // parts are multiplied (h - hi - lo is below 2^-16 |h|).
 __device__ __forceinline__ void load_t_frags(v8s (&tf)[2][2], const GemmArgs& g, int64_t blk0, int r32, int h) {
+    // 32-bit element offsets from the scalar base (T is far below 2^31
+    // elements), so no per-lane 64-bit address stays live across tiles
+    const uint8_t* t8 = reinterpret_cast<const uint8_t*>(g.t);
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-        const uint16_t* tb = g.t + (g.n_t == 1 ? 0 : (blk0 + p) * 1024) + r32;
+        const uint32_t base = (g.n_t == 1 ? 0u : (uint32_t)(blk0 + p) * 1024u) + (uint32_t)r32;
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) tf[p][s][e] = (short)tb[(16 * s + 8 * (e / 4) + 4 * h + e % 4) * 32];
+            for (int e = 0; e < 8; ++e)
+                tf[p][s][e] = *reinterpret_cast<const short*>(
+                    t8 + 2u * (base + (uint32_t)(16 * s + 8 * (e / 4) + 4 * h + e % 4) * 32u));
     }
 }
 
