@@ -342,15 +342,26 @@ __device__ __forceinline__ void store_bf16_half(uint8_t* region, F vals, uint16_
         *reinterpret_cast<v2u*>(wbase + q * 16) = o;
     }
     wave_lds_fence();
+    // Read back all of the wave's rows before the first store: one wait for
+    // the LDS instead of one per row.  The stores go through a descriptor
+    // whose record count ends at token row M, so the hardware drops rows past
+    // it without a branch per row; 32 rows x ld bf16 is far below 2^31 bytes
+    // (ld * K/2 < 2^31 with K >= 256).
     constexpr int kRowsPerInst = 64 / Q;               // Q lanes x 16 B per token row
+    constexpr int kIts = 32 / kRowsPerInst;
     const int q = lane % Q;
     const uint8_t* rbase = region + (lane / Q) * kRowPad + q * 16;
+    v4u rows[kIts];
 #pragma unroll
-    for (int it = 0; it < 32 / kRowsPerInst; ++it) {
-        const v4u v = *reinterpret_cast<const v4u*>(rbase + it * kRowsPerInst * kRowPad);
-        const int64_t tok = tok0 + it * kRowsPerInst + lane / Q;
-        if (tok < M) *reinterpret_cast<v4u*>(out + tok * ld + col0 + q * 8) = v;
-    }
+    for (int it = 0; it < kIts; ++it) rows[it] = *reinterpret_cast<const v4u*>(rbase + it * kRowsPerInst * kRowPad);
+    const int64_t valid = M - tok0 < 0 ? 0 : (M - tok0 < 32 ? M - tok0 : 32);
+    const __amdgpu_buffer_rsrc_t o =
+        buffer_rsrc(reinterpret_cast<const uint8_t*>(out + tok0 * ld + col0), valid * ld * 2);
+    const int row_bytes = (int)ld * 2;
+    const int off = (lane / Q) * row_bytes + q * 16;
+#pragma unroll
+    for (int it = 0; it < kIts; ++it)
+        __builtin_amdgcn_raw_buffer_store_b128(rows[it], o, off + it * kRowsPerInst * row_bytes, 0, 0);
     wave_lds_fence();
 }
 
