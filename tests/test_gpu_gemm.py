@@ -170,15 +170,17 @@ def test_swiglu_requant(with_bf16):
     assert exc_codes <= 0.001 * h_ref.size
 
 
+@pytest.mark.parametrize("k", [512, 256])
 @pytest.mark.parametrize("epilogue", ["none", "rmsnorm", "rmsnorm256", "swiglu_requant"])
-def test_persistent_many_tiles_ragged(epilogue):
+def test_persistent_many_tiles_ragged(epilogue, k):
     """More 256 x 256 tiles (4 x 80 = 320) than a persistent grid holds, so
     workgroups run several tiles in turn (the next tile's loads overlapping
     the epilogue), with a ragged last token tile (1000 = 3 * 256 + 232).  On
     a 256-CU device the plain and RMSNorm epilogues run the partial second
-    round (64 tiles) as 256 quarter tiles of 64 tokens."""
+    round (64 tiles) as 256 quarter tiles of 64 tokens.  K = 256 is the
+    shortest K: two stages, fewer than the quarter tiles keep in flight."""
     rng = np.random.default_rng(31)
-    m, n, k = 1000, 256 * 80, 512
+    m, n = 1000, 256 * 80
     rows = np.unique(np.concatenate([[0, 255, 256, 767, 768, 999], rng.choice(m, 40, replace=False)]))
     announce("gemm persistent", epilogue, m, n, k)
     if epilogue == "swiglu_requant":
