@@ -206,6 +206,31 @@ def test_persistent_many_tiles_ragged(epilogue, k):
         parity.assert_close(host(out)[rows], ref, parity.TOL_BF16, group=hd, what="persistent " + epilogue)
 
 
+@pytest.mark.parametrize("epilogue", ["none", "rmsnorm"])
+def test_quarter_tiles_two_per_workgroup(epilogue):
+    """384 tiles (4 x 96) on a 256-CU grid leave a partial round of 128
+    tiles: 512 quarter tiles, two per workgroup in turn (the second one's
+    loads start after the first one's epilogue has used the ring), K = 768
+    (six stages: one full turn of the quarter loop's unrolled body), and a
+    ragged last token tile."""
+    rng = np.random.default_rng(37)
+    m, n, k = 1000, 256 * 96, 768
+    rows = np.unique(np.concatenate([[0, 63, 64, 255, 768, 831, 832, 999], rng.choice(m, 40, replace=False)]))
+    announce("gemm quarter x2", epilogue, m, n, k)
+    ac, as_, bc, bs = _operands(rng, m, n, k)
+    c = ogemm.gemm(ac[rows], as_[rows], bc, bs)
+    if epilogue == "none":
+        out = ops.gemm_fp4_epilogue_none(*_dev_ops(ac, as_, bc, bs), out_dtype=torch.bfloat16)
+        parity.assert_close(host(out)[rows], c, parity.TOL_BF16, what="quarter x2 none")
+    else:
+        n_norm = n - 1024
+        norm_w = rng.uniform(0.5, 1.5, n_norm).astype(np.float32)
+        ref = ogemm.rmsnorm_head(c, 128, n_norm, norm_w.astype(np.float64), 1e-6)
+        out = ops.gemm_fp4_epilogue_rmsnorm_head(*_dev_ops(ac, as_, bc, bs), 128, n_norm,
+                                                 dev(norm_w, torch.float32), 1e-6, out_dtype=torch.bfloat16)
+        parity.assert_close(host(out)[rows], ref, parity.TOL_BF16, group=128, what="quarter x2 rmsnorm")
+
+
 # SwiGLU -> down-projection block transform -> MXFP4, fused in the epilogue
 
 def _check_fused(mx, y, c_g, c_u, t, rows=None, what="fused"):
