@@ -9,7 +9,8 @@
 // Activation quantisation is HBM-bound: 2 (bf16) or 4 (fp32) bytes in and
 // 17/32 byte out per element.  Four lanes share a 32-element block; each
 // lane takes 8 consecutive elements (16 B of bf16), so a wave reads 1 KiB of
-// contiguous memory per load; the input is read once (non-temporal loads).
+// contiguous memory per load; the input is read once (non-temporal loads for
+// bf16, whose 16-byte pieces cover whole lines per wave).
 // The block amax is reduced over the four lanes with DPP quad permutes.
 // Measured on 4096 x 4096 bf16: one 8-element unit per thread (many small
 // workgroups) beats 2, 4 or 8 units per thread with all loads issued first,
@@ -42,8 +43,12 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
                 xb[i][2 * j + 1] = v[j] & 0xFFFF0000u;
             }
         } else {
+            // fp32: a lane's 8 elements are two adjacent 16-byte pieces, so
+            // each load covers half of every line it touches; ordinary
+            // (cached) loads let the second one hit the line the first
+            // brought in (non-temporal ones fetched it twice)
             const v4u* p = reinterpret_cast<const v4u*>(static_cast<const float*>(x) + elem);
-            const v4u v0 = __builtin_nontemporal_load(p), v1 = __builtin_nontemporal_load(p + 1);
+            const v4u v0 = p[0], v1 = p[1];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 xb[i][j] = v0[j];
@@ -105,7 +110,7 @@ __global__ __launch_bounds__(256) void fake_quant_kernel(const void* __restrict_
         }
     } else {
         const v4u* p = reinterpret_cast<const v4u*>(static_cast<const float*>(x) + elem);
-        const v4u v0 = __builtin_nontemporal_load(p), v1 = __builtin_nontemporal_load(p + 1);
+        const v4u v0 = p[0], v1 = p[1];                 // cached: see quantize_kernel
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             xb[j] = v0[j];
@@ -141,9 +146,9 @@ __global__ __launch_bounds__(256) void fake_quant_kernel(const void* __restrict_
         for (int j = 0; j < 4; ++j) v[j] = (yb[2 * j] >> 16) | (yb[2 * j + 1] & 0xFFFF0000u);
         __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(static_cast<uint16_t*>(y) + elem));
     } else {
-        v4u* p = reinterpret_cast<v4u*>(static_cast<float*>(y) + elem);
-        __builtin_nontemporal_store((v4u){yb[0], yb[1], yb[2], yb[3]}, p);
-        __builtin_nontemporal_store((v4u){yb[4], yb[5], yb[6], yb[7]}, p + 1);
+        v4u* p = reinterpret_cast<v4u*>(static_cast<float*>(y) + elem);   // cached, as the loads
+        p[0] = (v4u){yb[0], yb[1], yb[2], yb[3]};
+        p[1] = (v4u){yb[4], yb[5], yb[6], yb[7]};
     }
 }
 

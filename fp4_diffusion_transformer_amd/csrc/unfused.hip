@@ -83,8 +83,10 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t* __restrict_
     const uint32_t pg = (o / group) * 2 * group + o % group;   // its gate column (g % 8 == 0)
     const uint16_t* src = c + (int64_t)row * row_chunks * 16 + pg;
     float gt[8], up[8], r[8];
-    unpack8(__builtin_nontemporal_load(reinterpret_cast<const v4u*>(src)), gt);
-    unpack8(__builtin_nontemporal_load(reinterpret_cast<const v4u*>(src + group)), up);
+    // cached loads: the gate and up loads each cover every other 64-byte
+    // half of the lines they touch (non-temporal loads fetched each line twice)
+    unpack8(*reinterpret_cast<const v4u*>(src), gt);
+    unpack8(*reinterpret_cast<const v4u*>(src + group), up);
 #pragma unroll
     for (int j = 0; j < 8; ++j) r[j] = gt[j] * __builtin_amdgcn_rcpf(1.0f + __expf(-gt[j])) * up[j];
     __builtin_nontemporal_store(pack8(r), reinterpret_cast<v4u*>(h + (int64_t)chunk * 8));
