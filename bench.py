@@ -38,6 +38,7 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_MXFP4_TFLOPS = 10100.0     # MI355X dense MXFP4 matrix peak
+PEAK_CLOCK_GHZ = 2.4            # the clock that peak is quoted at
 PEAK_HBM_GBS = 8000.0
 QUANT_BATCH = 20               # back-to-back launches timed for the quantisation figure
 HBM_ROTATE_BYTES = 512 << 20   # buffer sets rotated by an HBM-bound timing touch more than 2x the LLC
@@ -357,6 +358,7 @@ def main():
     from fp4_diffusion_transformer_amd import ops, workloads
 
     torch.cuda.init()
+    clk_idle = ops.shader_clock_ghz(1, 64)   # one workgroup, before any load (the shader-clock probe)
     if args.calib_mib:
         buf = torch.empty(args.calib_mib << 18, dtype=torch.float32, device="cuda")
         buf.fill_(1.0)                       # writes calib_mib MiB
@@ -403,6 +405,22 @@ def main():
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the clock under a sustained FP4 MFMA load: right after the timed region,
+    # the probe loads every CU with FP4 MFMAs for about a millisecond (the
+    # steps' own clock, read inside the GEMM the same way in a timing copy,
+    # agrees within a few per cent); its MFMA rate is the box's practical
+    # matrix ceiling at that clock
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    probe = torch.zeros(12 * cus, dtype=torch.int64, device="cuda")
+    p_iters = 3000
+    pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pe0.record()
+    ops.clock_probe(probe, cus, p_iters)
+    pe1.record()
+    torch.cuda.synchronize()
+    clk_load = float(np.median(ops.clock_ghz(probe, cus)))
+    mfma_pf = 2.0 * 32 * 32 * 64 * 16 * p_iters * 4 * cus / (pe0.elapsed_time(pe1) * 1e-3) / 1e15
+    del probe
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
     flops = sum(L.flops for L in layers)
@@ -429,7 +447,10 @@ def main():
     out_kind = 1 if (Ld.out is not None or Ld.unfused) else 0
     kt, ring = Ld.k // 128, 3
     epi_name = "none" if Ld.unfused else Ld.wl.epilogue + ("_transform" if Ld.next_t is not None else "")
-    kernel_key = "gemm_%s<%d,%d,%d>" % (epi_name, out_kind, ring, (kt - ring + 1) % ring)
+    peel = (kt - ring + 1) % ring                  # as the library picks it: a whole ring turn
+    if peel == 0 and kt - ring + 1 >= ring:        # rather than none when the loop would start at 0
+        peel = ring
+    kernel_key = "gemm_%s<%d,%d,%d>" % (epi_name, out_kind, ring, peel)
 
     out = {
         "metric": "fused MXFP4 GEMM+epilogue TFLOPS and % of MXFP4 peak at DiT 1K shapes",
@@ -454,6 +475,18 @@ def main():
                        for L in layers],
             "pct_of_mxfp4_peak": round(100.0 * tflops / PEAK_MXFP4_TFLOPS, 2),
             "wall_s_timed": round(wall, 3),
+        },
+        "clock": {
+            "method": "shader-clock probe: s_memtime against the 100 MHz s_memrealtime around FP4 MFMAs "
+                      "(32x32x64, pseudo-random operands); idle: one workgroup before any work; under load: "
+                      "one workgroup per CU for about 1 ms right after the timed region, median over waves",
+            "shader_ghz_idle": round(clk_idle, 3),
+            "shader_ghz_fp4_mfma_load": round(clk_load, 3),
+            "published_max_ghz": PEAK_CLOCK_GHZ,
+            "mfma_only_pflops_at_that_clock": round(mfma_pf, 3),
+            "pct_of_mxfp4_peak_at_measured_clock": round(
+                100.0 * tflops / (PEAK_MXFP4_TFLOPS * clk_load / PEAK_CLOCK_GHZ), 2),
+            "dominant_gemm_pct_of_mfma_only_rate": round(100.0 * achieved / (mfma_pf * 1e3), 2),
         },
         "roofline": {
             "kernel": kernel_key + " (%s, M=%d N=%d K=%d)" % (Ld.name, Ld.m, Ld.n, Ld.k),

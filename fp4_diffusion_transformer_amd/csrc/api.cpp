@@ -300,4 +300,11 @@ fp4dit_status fp4dit_etd_coefficients(double alpha_s, double sigma_s, double alp
     return FP4DIT_OK;
 }
 
+fp4dit_status fp4dit_clock_probe(uint64_t* out, int32_t workgroups, int32_t iters, hipStream_t stream) {
+    if (!out) return FP4DIT_E_NULL;
+    if (reinterpret_cast<uintptr_t>(out) % 8 != 0) return FP4DIT_E_ALIGN;
+    if (workgroups < 1 || workgroups > 65536 || iters < 1 || iters > (1 << 20)) return FP4DIT_E_SHAPE;
+    return launched(fp4dit::launch_clock_probe(out, workgroups, iters, stream));
+}
+
 }  // extern "C"

@@ -56,6 +56,11 @@ hipError_t launch_etd2(const void* x, const void* x0, const void* x0_prev, int64
 hipError_t launch_richardson(const void* fine, const void* coarse, int64_t n, int storage, float scale, void* out,
                              hipStream_t stream);
 
+// Shader-clock probe (measurement): per wave w of `workgroups` x 4 waves,
+// out[3w] shader-clock ticks and out[3w + 1] ticks of the 100 MHz counter
+// over `iters` rounds of 16 FP4 MFMAs, out[3w + 2] a checksum.
+hipError_t launch_clock_probe(uint64_t* out, int workgroups, int iters, hipStream_t stream);
+
 // Interleave group of the SwiGLU epilogue: channel blocks of 32 alternate
 // gate / up, matching one 32x32 MFMA output block per half.
 constexpr int kSwigluGroup = 32;

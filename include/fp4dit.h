@@ -348,6 +348,22 @@ fp4dit_status fp4dit_etd_coefficients(double alpha_s, double sigma_s, double alp
                                       int32_t order, int32_t first_step, double* decay, double* c0,
                                       double* c1);
 
+/*
+ * Measurement helper, no step of the method: the shader clock under a
+ * scaled FP4 MFMA load.  `workgroups` workgroups of 4 waves (one per CU
+ * loads the whole chip, as the persistent GEMM does) each run `iters`
+ * rounds of 16 independent 32x32x64 FP4 MFMAs on pseudo-random operands.
+ * Wave w writes, to the caller-owned device buffer `out` (3 uint64 per
+ * wave, 8-byte aligned): out[3w] the ticks of the shader-clock counter
+ * (s_memtime) and out[3w + 1] those of the constant 100 MHz counter
+ * (s_memrealtime) over its MFMAs, out[3w + 2] a checksum.  Its clock in GHz
+ * is 0.1 * out[3w] / out[3w + 1].  Enqueued on `stream`; the caller
+ * synchronises.  Returns FP4DIT_E_NULL for a NULL `out`, FP4DIT_E_ALIGN for
+ * a misaligned one, FP4DIT_E_SHAPE unless 1 <= workgroups <= 65536 and
+ * 1 <= iters <= 2^20.
+ */
+fp4dit_status fp4dit_clock_probe(uint64_t* out, int32_t workgroups, int32_t iters, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,7 +37,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     raw = ctypes.CDLL(ops.library_path())
     for n in names:
         assert hasattr(raw, n), n
@@ -156,6 +156,16 @@ def test_sampler_validation(L):
     assert e2(P, P + 4096, None, 100, BF16, 0.5, 0.3, 0.1, P + 8192, None) == E_NULL
     assert rc(P, P + 4096, 100, F32, 1.0, P + 8192, None) == E_UNSUP          # scale 1
     assert rc(None, None, 0, F32, 2.0, None, None) == OK
+
+
+def test_clock_probe_validation(L):
+    c = L.fp4dit_clock_probe
+    assert c(None, 1, 100, None) == E_NULL
+    assert c(P + 4, 1, 100, None) == E_ALIGN
+    assert c(P, 0, 100, None) == E_SHAPE
+    assert c(P, 65537, 100, None) == E_SHAPE
+    assert c(P, 1, 0, None) == E_SHAPE
+    assert c(P, 1, (1 << 20) + 1, None) == E_SHAPE
 
 
 def test_etd_coefficients_host_logic(L):
