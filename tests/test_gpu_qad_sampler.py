@@ -179,3 +179,35 @@ def test_etd1_sampler_loop_is_exact_for_a_constant_prediction():
     exact = (s1 / s0) * xh + s1 * (a1 / s1 - a0 / s0) * x0h
     g = x.cpu().numpy().astype(np.float64)
     assert np.max(np.abs(g - exact)) <= 1e-5 * (np.max(np.abs(xh)) + np.max(np.abs(x0h)))
+
+
+# ----------------------------------------------------- at the bench's sizes --
+def test_fake_quant_bench_shape_bit_exact():
+    """The QAD forward at the size bench.py times (4096 x 3072 bf16 -> bf16),
+    every element against the oracle."""
+    rng = np.random.default_rng(101)
+    x = rng.standard_normal((4096, 3072)) * 2.0 ** rng.integers(-8, 9, (4096, 1))
+    xd = dev(x, torch.bfloat16)
+    x_exact = xd.float().cpu().numpy().astype(np.float64)
+    announce("fake quant bench shape", x.shape)
+    y = ops.fake_quantize_mxfp4(xd, y_dtype=torch.bfloat16)
+    assert np.array_equal(_bits(y), _ref_bits(qad.fake_quantize(x_exact), torch.bfloat16))
+
+
+def test_sampler_updates_bench_shape():
+    """ETD1, ETD2 and the Richardson combine on the latent bench.py times
+    (16 latents of 16 x 128 x 128 fp32), every element within the bound."""
+    n = 16 * 16 * 128 * 128
+    rng = np.random.default_rng(102)
+    (x, xh), (x0, x0h), (xp, xph) = (_stored(rng, n, torch.float32) for _ in range(3))
+    d1, c, _ = ops.etd_coefficients(*_vp(0.6), *_vp(0.5), order=1)
+    d, c0, c1 = ops.etd_coefficients(*_vp(0.6), *_vp(0.5), order=2, first_step=False)
+    k = [float(np.float32(v)) for v in (d1, c, d, c0, c1)]
+    announce("sampler bench shape", n)
+    _check(ops.etd1_update(x, x0, d1, c), sampler.etd1_update(xh, x0h, k[0], k[1]),
+           np.abs(k[0] * xh) + np.abs(k[1] * x0h), torch.float32, "etd1 bench shape")
+    _check(ops.etd2_update(x, x0, xp, d, c0, c1), sampler.etd2_update(xh, x0h, xph, k[2], k[3], k[4]),
+           np.abs(k[2] * xh) + np.abs(k[3] * x0h) + np.abs(k[4] * xph), torch.float32, "etd2 bench shape")
+    out = ops.richardson_combine(x, x0, 2.0)
+    mag = (np.abs(2.0 * xh) + np.abs(x0h)) + np.abs(sampler.richardson_combine(xh, x0h, 2.0))
+    _check(out, sampler.richardson_combine(xh, x0h, 2.0), mag, torch.float32, "richardson bench shape")
