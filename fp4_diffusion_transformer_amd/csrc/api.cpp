@@ -4,6 +4,7 @@
 // other than FP4DIT_E_LAUNCH means nothing was enqueued.
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 
 #include "../../include/fp4dit.h"
 #include "launch.hpp"
@@ -25,6 +26,15 @@ bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
 bool valid_layout(fp4dit_layout l) { return l == FP4DIT_MX_ROWMAJOR || l == FP4DIT_MX_TILED; }
 fp4dit_status launched(hipError_t e) { return e == hipSuccess ? FP4DIT_OK : FP4DIT_E_LAUNCH; }
 
+// Every matrix size is below 2^31, so a product of two sizes (times a few
+// bytes) fits in int64 before the finer limits below are checked.
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+bool dims_ok(std::initializer_list<int64_t> dims) {
+    for (int64_t d : dims)
+        if (d > kMaxDim) return false;
+    return true;
+}
+
 // Byte offsets inside the GEMM operands are 32-bit (tiled buffers are padded
 // to an even number of rows).
 constexpr int64_t kMaxOperandBytes = (int64_t(1) << 31) - 1;
@@ -36,7 +46,7 @@ bool requant_fits(int64_t M, int64_t N) {
 
 fp4dit_status check_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
                          const uint8_t* bc, const uint8_t* bs) {
-    if (M < 0 || N <= 0 || K <= 0) return FP4DIT_E_SHAPE;
+    if (M < 0 || N <= 0 || K <= 0 || !dims_ok({M, N, K})) return FP4DIT_E_SHAPE;
     if (N % kGemmNMultiple != 0 || K % kGemmKMultiple != 0) return FP4DIT_E_SHAPE;
     if ((M + 1) * (K / 2) > kMaxOperandBytes || N * (K / 2) > kMaxOperandBytes) return FP4DIT_E_SHAPE;
     if (M == 0) return FP4DIT_OK;
@@ -67,6 +77,7 @@ fp4dit_status fp4dit_quantize_mxfp4(const void* x, fp4dit_dtype x_dtype, int64_t
                                     uint8_t* codes, uint8_t* scales, fp4dit_layout layout, hipStream_t stream) {
     if (!valid_dtype(x_dtype) || !valid_layout(layout)) return FP4DIT_E_UNSUPPORTED;
     if (rows < 0 || cols < 0 || cols % (layout == FP4DIT_MX_TILED ? 128 : 32) != 0) return FP4DIT_E_SHAPE;
+    if (!dims_ok({rows, cols})) return FP4DIT_E_SHAPE;
     if (rows == 0 || cols == 0) return FP4DIT_OK;
     if (rows * (cols / 32) >= (int64_t(1) << 32)) return FP4DIT_E_SHAPE;
     if (!x || !codes || !scales) return FP4DIT_E_NULL;
@@ -81,7 +92,7 @@ fp4dit_status fp4dit_block_transform(const void* x, fp4dit_dtype x_dtype, int64_
     if (!valid_dtype(x_dtype) || (y && !valid_dtype(y_dtype))) return FP4DIT_E_UNSUPPORTED;
     if ((codes == nullptr) != (scales == nullptr)) return FP4DIT_E_UNSUPPORTED;
     if (codes && !valid_layout(layout)) return FP4DIT_E_UNSUPPORTED;
-    if (rows < 0 || cols < 0 || cols % 32 != 0) return FP4DIT_E_SHAPE;
+    if (rows < 0 || cols < 0 || cols % 32 != 0 || !dims_ok({rows, cols})) return FP4DIT_E_SHAPE;
     if (codes && layout == FP4DIT_MX_TILED && cols % 128 != 0) return FP4DIT_E_SHAPE;
     if (n_t != 1 && n_t != cols / 32) return FP4DIT_E_SHAPE;
     if (rows == 0 || cols == 0) return FP4DIT_OK;
@@ -97,7 +108,7 @@ fp4dit_status fp4dit_block_transform(const void* x, fp4dit_dtype x_dtype, int64_
 
 fp4dit_status fp4dit_fold_inverse_transform(const float* w, int64_t K, int64_t N, const uint16_t* t_bf16,
                                             int64_t n_t, float* w_out, hipStream_t stream) {
-    if (K < 0 || N < 0 || K % 32 != 0) return FP4DIT_E_SHAPE;
+    if (K < 0 || N < 0 || K % 32 != 0 || !dims_ok({K, N})) return FP4DIT_E_SHAPE;
     if (n_t != 1 && n_t != K / 32) return FP4DIT_E_SHAPE;
     if (K == 0 || N == 0) return FP4DIT_OK;
     if (K / 32 > 65535) return FP4DIT_E_SHAPE;
@@ -113,6 +124,7 @@ fp4dit_status fp4dit_pack_weight(const void* w, fp4dit_dtype w_dtype, int64_t K,
     if (!valid_dtype(w_dtype) || !valid_layout(layout)) return FP4DIT_E_UNSUPPORTED;
     if (interleave_group < 0) return FP4DIT_E_UNSUPPORTED;
     if (K < 0 || N < 0 || K % (layout == FP4DIT_MX_TILED ? 128 : 32) != 0) return FP4DIT_E_SHAPE;
+    if (!dims_ok({K, N})) return FP4DIT_E_SHAPE;
     if (interleave_group > 0 && N % (2 * (int64_t)interleave_group) != 0) return FP4DIT_E_SHAPE;
     if (K == 0 || N == 0) return FP4DIT_OK;
     if (K / 32 > 65535) return FP4DIT_E_SHAPE;
@@ -198,7 +210,7 @@ fp4dit_status fp4dit_rmsnorm_head(const uint16_t* x, int64_t rows, int64_t cols,
                                   hipStream_t stream) {
     if (head_dim != 128 && head_dim != 256) return FP4DIT_E_UNSUPPORTED;
     if (!(eps >= 0.0f) || !std::isfinite(eps)) return FP4DIT_E_UNSUPPORTED;
-    if (rows < 0 || cols < 0 || cols % head_dim != 0) return FP4DIT_E_SHAPE;
+    if (rows < 0 || cols < 0 || cols % head_dim != 0 || !dims_ok({rows, cols})) return FP4DIT_E_SHAPE;
     if (n_norm_cols < 0 || n_norm_cols > cols || n_norm_cols % head_dim != 0) return FP4DIT_E_SHAPE;
     if (rows == 0 || cols == 0) return FP4DIT_OK;
     if (rows * (cols / 8) >= (int64_t(1) << 32)) return FP4DIT_E_SHAPE;
@@ -210,7 +222,8 @@ fp4dit_status fp4dit_rmsnorm_head(const uint16_t* x, int64_t rows, int64_t cols,
 fp4dit_status fp4dit_swiglu(const uint16_t* c, int64_t rows, int64_t n_phys, int32_t group, uint16_t* h,
                             hipStream_t stream) {
     if (group <= 0 || group % 8 != 0) return FP4DIT_E_UNSUPPORTED;
-    if (rows < 0 || n_phys < 0 || n_phys % (2 * int64_t(group)) != 0) return FP4DIT_E_SHAPE;
+    if (rows < 0 || n_phys < 0 || n_phys % (2 * int64_t(group)) != 0 || !dims_ok({rows, n_phys}))
+        return FP4DIT_E_SHAPE;
     if (rows == 0 || n_phys == 0) return FP4DIT_OK;
     if (rows * (n_phys / 16) >= (int64_t(1) << 32)) return FP4DIT_E_SHAPE;
     if (!c || !h) return FP4DIT_E_NULL;
@@ -223,7 +236,7 @@ fp4dit_status fp4dit_swiglu(const uint16_t* c, int64_t rows, int64_t n_phys, int
 fp4dit_status fp4dit_fake_quantize_mxfp4(const void* x, fp4dit_dtype x_dtype, int64_t rows, int64_t cols,
                                          void* y, fp4dit_dtype y_dtype, hipStream_t stream) {
     if (!valid_dtype(x_dtype) || !valid_dtype(y_dtype)) return FP4DIT_E_UNSUPPORTED;
-    if (rows < 0 || cols < 0 || cols % 32 != 0) return FP4DIT_E_SHAPE;
+    if (rows < 0 || cols < 0 || cols % 32 != 0 || !dims_ok({rows, cols})) return FP4DIT_E_SHAPE;
     if (rows == 0 || cols == 0) return FP4DIT_OK;
     if (rows * (cols / 8) >= (int64_t(1) << 40)) return FP4DIT_E_SHAPE;
     if (!x || !y) return FP4DIT_E_NULL;

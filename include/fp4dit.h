@@ -42,6 +42,9 @@
  *   host threads on different streams are safe.
  * - Zero-sized work (rows == 0, M == 0) returns FP4DIT_OK and enqueues
  *   nothing; the other sizes must still be valid.
+ * - Every matrix size (rows, cols, M, N, K) must be below 2^31
+ *   (FP4DIT_E_SHAPE otherwise); entry points state tighter limits where
+ *   their kernels need them.
  *
  * Citations name the web pages this library implements: "fal" is the fal
  * page "Serving sub-second Ideogram v4 without quality loss" (FP4 execution

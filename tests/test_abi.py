@@ -158,6 +158,20 @@ def test_sampler_validation(L):
     assert rc(None, None, 0, F32, 2.0, None, None) == OK
 
 
+def test_sizes_too_large_for_int64_products(L):
+    """Sizes whose products would overflow int64 are rejected before any
+    arithmetic on them (each size must be below 2^31)."""
+    big = 1 << 40
+    assert L.fp4dit_quantize_mxfp4(P, BF16, big, big, P, P, ROWMAJOR, None) == E_SHAPE
+    assert L.fp4dit_fake_quantize_mxfp4(P, BF16, big, big, P, BF16, None) == E_SHAPE
+    assert L.fp4dit_rmsnorm_head(P, big, 128 * big, 128, 0, None, 1e-6, P, None) == E_SHAPE
+    assert L.fp4dit_swiglu(P, big, 64 * big, 32, P, None) == E_SHAPE
+    assert L.fp4dit_gemm_fp4_epilogue_none(big, 256, 256, P, P, P, P, P, BF16, None) == E_SHAPE
+    assert L.fp4dit_pack_weight(P, F32, 128 * big, big, 0, P, P, TILED, None) == E_SHAPE
+    assert L.fp4dit_block_transform(P, BF16, big, 128 * big, P, 1, None, BF16, P, P, TILED, None) == E_SHAPE
+    assert L.fp4dit_fold_inverse_transform(P, 32 * big, big, P, 1, P + 64, None) == E_SHAPE
+
+
 def test_clock_probe_validation(L):
     c = L.fp4dit_clock_probe
     assert c(None, 1, 100, None) == E_NULL
