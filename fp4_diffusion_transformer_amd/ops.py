@@ -145,11 +145,49 @@ def mx_empty(rows, cols, layout="tiled", device="cuda"):
     return MxTensor(codes, scales, rows, cols, layout)
 
 
+def _mx_bytes(rows, cols, layout):
+    if layout == "tiled":
+        return _round_up(rows, 2) * (cols // 2), _round_up(rows, 32) * (cols // 32)
+    return rows * (cols // 2), rows * (cols // 32)
+
+
+def _mx_check(mx: MxTensor, rows, cols, name):
+    """An MxTensor the library will read or write as [rows, cols]: uint8,
+    contiguous device buffers at least as large as its layout needs (the
+    C ABI takes bare pointers and cannot check sizes)."""
+    if mx.layout not in _LAYOUTS:
+        raise ValueError(name + ".layout must be 'tiled' or 'rowmajor'")
+    if mx.rows != rows or mx.cols != cols:
+        raise ValueError("%s is [%d, %d], expected [%d, %d]" % (name, mx.rows, mx.cols, rows, cols))
+    need = _mx_bytes(rows, cols, mx.layout)
+    for t, nm, n in ((mx.codes, name + ".codes", need[0]), (mx.scales, name + ".scales", need[1])):
+        _dev(t, nm)
+        if t.dtype != torch.uint8:
+            raise ValueError(nm + " must be uint8")
+        if t.numel() < n:
+            raise ValueError("%s holds %d bytes, needs %d" % (nm, t.numel(), n))
+    return mx
+
+
+def _out_check(t, shape, dtypes, name):
+    """A caller-given output tensor: on the device, contiguous, of `shape`
+    and one of `dtypes`."""
+    _dev(t, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype not in dtypes:
+        raise ValueError("%s must be one of %s, got %s" % (name, dtypes, t.dtype))
+    return t
+
+
+_F32_BF16 = (torch.float32, torch.bfloat16)
+
+
 def quantize_mxfp4(x, layout="tiled", out: Optional[MxTensor] = None):
     """x [rows, cols] float32/bfloat16 -> MxTensor."""
     _dev(x, "x")
     rows, cols = x.shape
-    mx = out if out is not None else mx_empty(rows, cols, layout, x.device)
+    mx = _mx_check(out, rows, cols, "out") if out is not None else mx_empty(rows, cols, layout, x.device)
     _call("fp4dit_quantize_mxfp4", _ptr(x), _dtype_code(x.dtype), rows, cols, _ptr(mx.codes), _ptr(mx.scales),
           _LAYOUTS[mx.layout], _stream())
     return mx
@@ -169,9 +207,11 @@ def block_transform(x, t, y_dtype=None, quantize=True, layout="tiled", y=None, o
     rows, cols = x.shape
     if y is None and y_dtype is not None:
         y = torch.empty((rows, cols), dtype=y_dtype, device=x.device)
+    elif y is not None:
+        _out_check(y, (rows, cols), _F32_BF16, "y")
     mx = None
     if quantize:
-        mx = out if out is not None else mx_empty(rows, cols, layout, x.device)
+        mx = _mx_check(out, rows, cols, "out") if out is not None else mx_empty(rows, cols, layout, x.device)
     _call("fp4dit_block_transform", _ptr(x), _dtype_code(x.dtype), rows, cols, _ptr(t), t.shape[0],
           _ptr(y), _dtype_code(y.dtype) if y is not None else F32,
           _ptr(mx.codes) if mx else None, _ptr(mx.scales) if mx else None,
@@ -214,6 +254,8 @@ def _gemm_shapes(a: MxTensor, b: MxTensor):
         raise ValueError("GEMM operands must be in the tiled layout")
     if a.cols != b.cols:
         raise ValueError("A and B disagree on K")
+    _mx_check(a, a.rows, a.cols, "a")
+    _mx_check(b, b.rows, b.cols, "b")
     return a.rows, b.rows, a.cols
 
 
@@ -221,6 +263,7 @@ def gemm_fp4_epilogue_none(a: MxTensor, b: MxTensor, out_dtype=torch.bfloat16, o
     m, n, k = _gemm_shapes(a, b)
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=a.codes.device)
+    _out_check(out, (m, n), _F32_BF16, "out")
     _call("fp4dit_gemm_fp4_epilogue_none", m, n, k, _ptr(a.codes), _ptr(a.scales), _ptr(b.codes), _ptr(b.scales),
           _ptr(out), _dtype_code(out.dtype), _stream())
     return out
@@ -233,8 +276,11 @@ def gemm_fp4_epilogue_rmsnorm_head(a: MxTensor, b: MxTensor, head_dim, n_norm_co
         _dev(norm_w, "norm_w")
         if norm_w.dtype != torch.float32:
             raise ValueError("norm_w must be float32")
+    if norm_w is not None and norm_w.numel() < int(n_norm_cols):
+        raise ValueError("norm_w holds %d gains, needs %d" % (norm_w.numel(), int(n_norm_cols)))
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=a.codes.device)
+    _out_check(out, (m, n), _F32_BF16, "out")
     _call("fp4dit_gemm_fp4_epilogue_rmsnorm_head", m, n, k, _ptr(a.codes), _ptr(a.scales), _ptr(b.codes),
           _ptr(b.scales), int(head_dim), int(n_norm_cols), _ptr(norm_w), float(eps), _ptr(out),
           _dtype_code(out.dtype), _stream())
@@ -250,9 +296,14 @@ def gemm_fp4_epilogue_swiglu(a: MxTensor, b: MxTensor, out_dtype=torch.bfloat16,
     h = out
     if h is None and out_dtype is not None:
         h = torch.empty((m, n // 2), dtype=out_dtype, device=a.codes.device)
+    elif h is not None:
+        _out_check(h, (m, n // 2), _F32_BF16, "out")
     mx = None
     if requant:
         mx = out_mx if out_mx is not None else mx_empty(m, n // 2, "tiled", a.codes.device)
+        if mx.layout != "tiled":
+            raise ValueError("the requantised output is tiled")
+        _mx_check(mx, m, n // 2, "out_mx")
     _call("fp4dit_gemm_fp4_epilogue_swiglu", m, n, k, _ptr(a.codes), _ptr(a.scales), _ptr(b.codes),
           _ptr(b.scales), _ptr(h), _dtype_code(h.dtype) if h is not None else F32,
           _ptr(mx.codes) if mx else None, _ptr(mx.scales) if mx else None, _stream())
@@ -271,7 +322,12 @@ def gemm_fp4_epilogue_swiglu_transform(a: MxTensor, b: MxTensor, t, y_dtype=None
         raise ValueError("t must be bfloat16")
     if y is None and y_dtype is not None:
         y = torch.empty((m, n // 2), dtype=y_dtype, device=a.codes.device)
+    elif y is not None:
+        _out_check(y, (m, n // 2), _F32_BF16, "y")
     mx = out_mx if out_mx is not None else mx_empty(m, n // 2, "tiled", a.codes.device)
+    if mx.layout != "tiled":
+        raise ValueError("the requantised output is tiled")
+    _mx_check(mx, m, n // 2, "out_mx")
     _call("fp4dit_gemm_fp4_epilogue_swiglu_transform", m, n, k, _ptr(a.codes), _ptr(a.scales), _ptr(b.codes),
           _ptr(b.scales), _ptr(t), t.shape[0], _ptr(y), _dtype_code(y.dtype) if y is not None else F32,
           _ptr(mx.codes), _ptr(mx.scales), _stream())
@@ -288,8 +344,11 @@ def rmsnorm_head(x, head_dim, n_norm_cols, norm_w, eps=1e-6, out=None):
         if norm_w.dtype != torch.float32:
             raise ValueError("norm_w must be float32")
     rows, cols = x.shape
+    if norm_w is not None and norm_w.numel() < int(n_norm_cols):
+        raise ValueError("norm_w holds %d gains, needs %d" % (norm_w.numel(), int(n_norm_cols)))
     if out is None:
         out = torch.empty_like(x)
+    _out_check(out, (rows, cols), (torch.bfloat16,), "out")
     _call("fp4dit_rmsnorm_head", _ptr(x), rows, cols, int(head_dim), int(n_norm_cols), _ptr(norm_w), float(eps),
           _ptr(out), _stream())
     return out
@@ -303,6 +362,7 @@ def swiglu(c, group, out=None):
     rows, n_phys = c.shape
     if out is None:
         out = torch.empty((rows, n_phys // 2), dtype=torch.bfloat16, device=c.device)
+    _out_check(out, (rows, n_phys // 2), (torch.bfloat16,), "out")
     _call("fp4dit_swiglu", _ptr(c), rows, n_phys, int(group), _ptr(out), _stream())
     return out
 
@@ -314,6 +374,7 @@ def fake_quantize_mxfp4(x, y_dtype=None, out=None):
     rows, cols = x.shape
     if out is None:
         out = torch.empty((rows, cols), dtype=y_dtype or x.dtype, device=x.device)
+    _out_check(out, (rows, cols), _F32_BF16, "out")
     _call("fp4dit_fake_quantize_mxfp4", _ptr(x), _dtype_code(x.dtype), rows, cols, _ptr(out),
           _dtype_code(out.dtype), _stream())
     return out
