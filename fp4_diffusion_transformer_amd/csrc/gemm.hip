@@ -39,6 +39,7 @@
 //   the same permutation, so the sum over K is unchanged.
 // * bf16 outputs go through LDS (after the main loop) so that every global
 //   store writes whole row segments.
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -1085,16 +1086,18 @@ void launch_epi(const GemmArgs& g, bool out_bf16, dim3 grid, hipStream_t stream)
 }
 
 // Compute units of the current device (cached per device).
+// CU count per device, cached (atomically: host threads may launch at once;
+// a race only makes two of them query the same value).
 int device_cus() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 hipError_t launch_gemm(const GemmArgs& g, int epi, bool out_bf16, hipStream_t stream) {

@@ -38,8 +38,9 @@
  * - Arguments are checked on the host before anything is enqueued.  A
  *   status other than FP4DIT_OK means nothing was enqueued, except
  *   FP4DIT_E_LAUNCH, which reports a failed kernel launch.  No exception
- *   crosses the ABI; there is no global mutable state, so calls from several
- *   host threads on different streams are safe.
+ *   crosses the ABI; the only global state is a per-device cache of the CU
+ *   count, kept in atomics, so calls from several host threads on different
+ *   streams are safe.
  * - Zero-sized work (rows == 0, M == 0) returns FP4DIT_OK and enqueues
  *   nothing; the other sizes must still be valid.
  * - Every matrix size (rows, cols, M, N, K) must be below 2^31
