@@ -321,10 +321,13 @@ __device__ __forceinline__ void tile_of(int bid, int nwg, int tiles_n, int tiles
 // that every global store writes whole row segments.  vals(q, v) gives the
 // lane's 4 fp32 values of 8-column chunk q (half h) for token tok0 + r32.
 // Token rows sit kRowPad = 16Q + 16 bytes apart: the 16-byte pad rotates
-// consecutive rows by four banks, so both the 8-byte writes (lanes = 32 rows
-// x 2 halves) and the 16-byte row reads are free of bank conflicts, and all
-// accesses of a lane share one base address (immediate offsets).  Only this
-// wave touches `region` (32 * kRowPad bytes).
+// consecutive rows by four banks, so the 16-byte row reads are free of bank
+// conflicts; the 8-byte writes put rows r and r + 16 on the same banks
+// (SQ_LDS_BANK_CONFLICT: about 8% of the RMSNorm GEMMs' LDS-active cycles).
+// An 8-byte pad with the rows read back in 8-byte halves took a third of
+// those conflicts away and no time.  All accesses of a lane share one base
+// address (immediate offsets).  Only this wave touches `region`
+// (32 * kRowPad bytes).
 template <int Q>
 constexpr int row_pad_bytes() { return Q * 16 + 16; }
 

@@ -2,6 +2,7 @@
 
 Usage (after the three profiling runs named in the summary header):
   python -m fp4_diffusion_transformer_amd.profsum TRACE_DIR FETCH_DIR WRITE_DIR OUT_TXT [CALIB_MIB] [CMDS]
+  python -m fp4_diffusion_transformer_amd.profsum --sq SQ_DIR OUT_TXT [CMDS]
 
 TRACE_DIR: `rocprofv3 --kernel-trace --stats --output-format csv` output;
 FETCH_DIR / WRITE_DIR: `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE`
@@ -13,6 +14,15 @@ a text file with the commands that produced the inputs, copied into OUT_TXT.
 Writes OUT_TXT (kernel time table + per-launch HBM traffic) and
 profiles/hbm_traffic.json (traffic per kernel, with the hash of the kernel
 sources it was taken on; bench.py reports it only while the hash matches).
+
+--sq: SQ_DIR is a `rocprofv3 --pmc` run (csv) of SQ_VALU_MFMA_BUSY_CYCLES,
+SQ_BUSY_CU_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_F6F4, SQ_INSTS_MFMA,
+SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE, SQ_INSTS_VALU, SQ_INSTS_LDS and
+GRBM_GUI_ACTIVE.  OUT_TXT gets, per GEMM kernel, the averages per dispatch:
+MFMA utilisation (MFMA busy cycles over 4 SIMDs x CU-busy cycles), the FP4
+work the MFMA counter implies (512 flops per MOP, to check against 2MNK),
+the bank-conflict share of LDS-active cycles, instruction counts, and the
+SGPRs, LDS bytes and scratch (spill) bytes of the dispatch.
 """
 
 import csv
@@ -105,5 +115,44 @@ def main(argv):
     print("\n".join(lines))
 
 
+def sq_main(argv):
+    sq_dir, out_txt = argv[2:4]
+    cmds = open(argv[4]).read().strip().splitlines() if len(argv) > 4 else []
+    path = _find(sq_dir, "*counter_collection.csv")
+    vals = defaultdict(lambda: defaultdict(list))
+    regs = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            key = kernel_key(row["Kernel_Name"])
+            if not key.startswith("gemm_"):
+                continue
+            vals[key][row["Counter_Name"]].append(float(row["Counter_Value"]))
+            regs[key] = (row.get("VGPR_Count"), row.get("Accum_VGPR_Count"), row.get("SGPR_Count"),
+                         row.get("LDS_Block_Size"), row.get("Scratch_Size"))
+    lines = ["# rocprofv3 SQ counters of bench.py's GEMM kernels (averages per dispatch)", ""]
+    lines += ["# " + c for c in cmds] + [""] if cmds else []
+    lines.append("source hash of fp4_diffusion_transformer_amd/csrc: " + source_hash())
+    lines.append("")
+    lines.append("%-28s %9s %11s %9s %11s %11s %11s %5s %7s %7s" % (
+        "kernel", "mfma_util", "fp4_gflop", "lds_conf", "mfma_insts", "valu_insts", "lds_insts",
+        "sgpr", "lds_B", "scratch"))
+    for key in sorted(vals):
+        d = {c: sum(v) / len(v) for c, v in vals[key].items()}
+        busy = d.get("SQ_BUSY_CU_CYCLES", 0.0)
+        util = d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (4 * busy) if busy else float("nan")
+        lds = d.get("SQ_LDS_IDX_ACTIVE", 0.0)
+        conf = d.get("SQ_LDS_BANK_CONFLICT", 0.0) / lds if lds else 0.0
+        _, _, sg, ldsb, scr = regs[key]
+        lines.append("%-28s %9.3f %11.1f %9.4f %11.0f %11.0f %11.0f %5s %7s %7s" % (
+            key[:28], util, d.get("SQ_INSTS_VALU_MFMA_MOPS_F6F4", 0.0) * 512 / 1e9, conf,
+            d.get("SQ_INSTS_MFMA", 0.0), d.get("SQ_INSTS_VALU", 0.0), d.get("SQ_INSTS_LDS", 0.0), sg, ldsb, scr))
+    with open(out_txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
-    main(sys.argv)
+    if len(sys.argv) > 1 and sys.argv[1] == "--sq":
+        sq_main(sys.argv)
+    else:
+        main(sys.argv)
