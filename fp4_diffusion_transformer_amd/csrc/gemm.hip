@@ -323,7 +323,7 @@ __device__ __forceinline__ void tile_of(int bid, int nwg, int tiles_n, int tiles
 // Token rows sit kRowPad = 16Q + 16 bytes apart: the 16-byte pad rotates
 // consecutive rows by four banks, so the 16-byte row reads are free of bank
 // conflicts; the 8-byte writes put rows r and r + 16 on the same banks
-// (SQ_LDS_BANK_CONFLICT: about 8% of the RMSNorm GEMMs' LDS-active cycles).
+// (SQ_LDS_BANK_CONFLICT: about 12% of the RMSNorm GEMMs' LDS-active cycles).
 // An 8-byte pad with the rows read back in 8-byte halves took a third of
 // those conflicts away and no time.  All accesses of a lane share one base
 // address (immediate offsets).  Only this wave touches `region`
