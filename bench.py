@@ -351,7 +351,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
-              "(the path shards by tokens with no exchange, see DESIGN.md)" % args.gpus, file=sys.stderr)
+              "(the path shards by tokens with no exchange between GPUs)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
     sys.path.insert(0, ROOT)
