@@ -350,7 +350,7 @@ def aux_kernels(torch, ops, workloads):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+        print("bench.py: the path runs on one GPU; --gpus %d is not supported "
               "(the path shards by tokens with no exchange between GPUs)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
