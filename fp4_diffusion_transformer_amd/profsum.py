@@ -83,10 +83,14 @@ def main(argv):
     copy_bytes = copy_mib << 20
 
     def calib(per_kernel, tag):
+        # the calibration kernel is the largest dispatch of its kind (other
+        # small fills, e.g. of a zeroed index buffer, share the name)
+        best = None
         for name, vals in per_kernel.items():
             if tag in name:
-                return copy_bytes / (vals[0] * 1024.0)
-        return None
+                v = max(vals)
+                best = v if best is None or v > best else best
+        return copy_bytes / (best * 1024.0) if best else None
     f_fac, w_fac = calib(fetch, "reduce_kernel"), calib(write, "FillFunctor")
     lines = ["# rocprofv3 kernel statistics and HBM traffic of bench.py", ""]
     lines += ["# " + c for c in cmds] + [""] if cmds else []
