@@ -48,7 +48,28 @@ def build(verbose=True):
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)
+    build_c_consumer(verbose)
     return LIB
+
+
+C_CONSUMER_SRC = os.path.join(ROOT, "tests", "c_consumer.c")
+C_CONSUMER = os.path.join(ROOT, "tests", "c_consumer")
+
+
+def build_c_consumer(verbose=True):
+    """The plain C program of the C-ABI test, linked against the library
+    (C99 with gcc: the header is usable from C)."""
+    if not os.path.exists(C_CONSUMER_SRC):
+        return None
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROOT, "include"),
+           "-I/opt/rocm/include", C_CONSUMER_SRC, "-o", C_CONSUMER, "-L" + HERE, "-lfp4dit", "-L/opt/rocm/lib",
+           "-lamdhip64", "-Wl,-rpath,$ORIGIN/../fp4_diffusion_transformer_amd", "-Wl,-rpath,/opt/rocm/lib"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("gcc failed on the C consumer:\n" + r.stderr)
+    if verbose:
+        print("built", C_CONSUMER)
+    return C_CONSUMER
 
 
 if __name__ == "__main__":
