@@ -7,12 +7,15 @@
  * tests/test_gpu_c_consumer.py runs it and checks its output against the
  * oracle.
  *
- *   c_consumer DIR M N K
+ *   c_consumer DIR M N K [swiglu]
  *
- * reads DIR/x.bin (bf16 bits, [M][K]), DIR/w.bin (fp32, [K][N]) and
- * DIR/g.bin (fp32 gains, [N]); writes DIR/y.bin (bf16 bits, [M][N]) =
- * per-head (128) RMSNorm of the MXFP4 GEMM, gains on every column,
- * eps 1e-6.  Exit status 0 on success; a failing call prints its status.
+ * reads DIR/x.bin (bf16 bits, [M][K]) and DIR/w.bin (fp32, [K][N]).
+ * Default: also DIR/g.bin (fp32 gains, [N]); writes DIR/y.bin (bf16 bits,
+ * [M][N]) = per-head (128) RMSNorm of the MXFP4 GEMM, gains on every
+ * column, eps 1e-6.  "swiglu": w is [gate | up] (N/2 columns each), packed
+ * with the library's interleave group; writes the MXFP4 requantisation of
+ * SwiGLU(x.W) as DIR/codes.bin and DIR/scales.bin (MX_TILED, [M][N/2]).
+ * Exit status 0 on success; a failing call prints its status.
  */
 #include <stdio.h>
 #include <stdlib.h>
@@ -53,15 +56,16 @@ static void* read_file(const char* dir, const char* name, size_t bytes) {
 static size_t round_up(size_t v, size_t m) { return (v + m - 1) / m * m; }
 
 int main(int argc, char** argv) {
-    if (argc != 5) {
-        fprintf(stderr, "usage: %s DIR M N K\n", argv[0]);
+    if (argc != 5 && argc != 6) {
+        fprintf(stderr, "usage: %s DIR M N K [swiglu]\n", argv[0]);
         return 2;
     }
     const char* dir = argv[1];
     const int64_t M = atoll(argv[2]), N = atoll(argv[3]), K = atoll(argv[4]);
+    const int swiglu = argc == 6;
     uint16_t* x = read_file(dir, "x.bin", (size_t)(M * K) * 2);
     float* w = read_file(dir, "w.bin", (size_t)(K * N) * 4);
-    float* g = read_file(dir, "g.bin", (size_t)N * 4);
+    float* g = swiglu ? malloc(4) : read_file(dir, "g.bin", (size_t)N * 4);
     if (!x || !w || !g) {
         fprintf(stderr, "cannot read the inputs in %s\n", dir);
         return 1;
@@ -86,6 +90,34 @@ int main(int argc, char** argv) {
     HIP_OK(hipMemcpyAsync(dg, g, (size_t)N * 4, hipMemcpyHostToDevice, st));
 
     FP4_OK(fp4dit_quantize_mxfp4(dx, FP4DIT_BF16, M, K, dac, das, FP4DIT_MX_TILED, st));
+    if (swiglu) {
+        const int64_t nh = N / 2;
+        const size_t h_codes = round_up((size_t)M, 2) * (size_t)(nh / 2), h_scales = round_up((size_t)M, 32) * (size_t)(nh / 32);
+        uint8_t *dhc, *dhs;
+        HIP_OK(hipMalloc((void**)&dhc, h_codes));
+        HIP_OK(hipMalloc((void**)&dhs, h_scales));
+        FP4_OK(fp4dit_pack_weight(dw, FP4DIT_F32, K, N, fp4dit_swiglu_interleave_group(), dbc, dbs,
+                                  FP4DIT_MX_TILED, st));
+        FP4_OK(fp4dit_gemm_fp4_epilogue_swiglu(M, N, K, dac, das, dbc, dbs, NULL, FP4DIT_BF16, dhc, dhs, st));
+        uint8_t* hc = malloc(h_codes);
+        uint8_t* hs = malloc(h_scales);
+        if (!hc || !hs) return 1;
+        HIP_OK(hipMemcpyAsync(hc, dhc, h_codes, hipMemcpyDeviceToHost, st));
+        HIP_OK(hipMemcpyAsync(hs, dhs, h_scales, hipMemcpyDeviceToHost, st));
+        HIP_OK(hipStreamSynchronize(st));
+        char path[4096];
+        snprintf(path, sizeof path, "%s/codes.bin", dir);
+        FILE* f = fopen(path, "wb");
+        if (!f || fwrite(hc, 1, h_codes, f) != h_codes) return 1;
+        fclose(f);
+        snprintf(path, sizeof path, "%s/scales.bin", dir);
+        f = fopen(path, "wb");
+        if (!f || fwrite(hs, 1, h_scales, f) != h_scales) return 1;
+        fclose(f);
+        hipFree(dhc); hipFree(dhs);
+        free(hc); free(hs);
+        return 0;
+    }
     FP4_OK(fp4dit_pack_weight(dw, FP4DIT_F32, K, N, 0, dbc, dbs, FP4DIT_MX_TILED, st));
     FP4_OK(fp4dit_gemm_fp4_epilogue_rmsnorm_head(M, N, K, dac, das, dbc, dbs, 128, N, (const float*)dg, 1e-6f,
                                                  dy, FP4DIT_BF16, st));
