@@ -363,9 +363,16 @@ __device__ __forceinline__ void store_bf16_half(uint8_t* region, F vals, uint16_
         buffer_rsrc(reinterpret_cast<const uint8_t*>(out + tok0 * ld + col0), valid * ld * 2);
     const int row_bytes = (int)ld * 2;
     const int off = (lane / Q) * row_bytes + q * 16;
+    // Non-temporal (cache policy nt): the output is written once and not read
+    // back by this kernel.  Measured with four output buffers in rotation
+    // (more than the last-level cache holds): 4096x9216x3072 RMSNorm GEMM
+    // 70.6 -> 67.3 us, 4096x12288x4096 within 1%; with one output buffer,
+    // which stays cache-resident, within 1% for both.  The SwiGLU requant
+    // stores timed the same either way and keep the default policy.
+    constexpr int kStoreNt = 2;
 #pragma unroll
     for (int it = 0; it < kIts; ++it)
-        __builtin_amdgcn_raw_buffer_store_b128(rows[it], o, off + it * kRowsPerInst * row_bytes, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(rows[it], o, off + it * kRowsPerInst * row_bytes, 0, kStoreNt);
     wave_lds_fence();
 }
 
