@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 import torch
 
+import layout
 import parity
 from gpu_util import announce, dev, host
 from fp4_diffusion_transformer_amd import ops, workloads
@@ -59,12 +60,14 @@ def test_swiglu(rows, n_half, g):
     parity.assert_close(host(h), ref, parity.TOL_BF16, what="unfused swiglu")
 
 
-def test_unfused_chain_qkv_hd128_full_size():
-    """quantise -> GEMM (bf16 store) -> RMSNorm launch, at the QKV hd128
-    shape (4096 x 9216 x 3072); sampled rows against the oracle's RMSNorm of
-    the bf16-rounded GEMM output."""
-    wl = workloads.qkv_hd128()
-    announce("unfused chain qkv_hd128", wl.m, wl.n, wl.k)
+@pytest.mark.parametrize("make", [workloads.qkv_hd128, workloads.qkv_hd256], ids=["hd128", "hd256"])
+def test_unfused_chain_qkv_full_size(make):
+    """quantise -> GEMM (bf16 store) -> RMSNorm launch, at the QKV shapes
+    (4096 x 9216 x 3072 with hd 128, 4096 x 12288 x 4096 with hd 256);
+    sampled rows against the oracle's RMSNorm of the bf16-rounded GEMM
+    output."""
+    wl = make()
+    announce("unfused chain", wl.name, wl.m, wl.n, wl.k)
     a = ops.quantize_mxfp4(dev(wl.x, torch.bfloat16))
     b = ops.pack_weight(dev(wl.w, torch.float32))
     c = ops.gemm_fp4_epilogue_none(a, b, out_dtype=torch.bfloat16)
@@ -76,3 +79,40 @@ def test_unfused_chain_qkv_hd128_full_size():
     c_ref = obf16.round_bf16(ogemm.gemm(ac, as_, bc, bs))
     ref = ogemm.rmsnorm_head(c_ref, wl.head_dim, wl.n_norm, wl.norm_w.astype(np.float64), wl.eps)
     parity.assert_close(host(y)[rows], ref, parity.TOL_BF16, group=wl.head_dim, what="unfused chain")
+
+
+def test_unfused_chain_ffn_up_full_size():
+    """quantise -> GEMM over the interleaved [gate | up] weight (bf16 store)
+    -> SwiGLU launch -> quantise, at the FFN-up shape (4096 x 24576 x 3072).
+    Sampled rows: h against the oracle's SwiGLU of the bf16-rounded gate and
+    up outputs, and the MXFP4 codes of h within the rounding band of that
+    reference (h itself is a bf16 rounding of it)."""
+    wl = workloads.ffn_up_swiglu(requant=False)
+    g = ops.swiglu_interleave_group()
+    n_half = wl.w_gate.shape[1]
+    announce("unfused chain ffn_up", wl.m, 2 * n_half, wl.k)
+    a = ops.quantize_mxfp4(dev(wl.x, torch.bfloat16))
+    b = ops.pack_weight(dev(np.concatenate([wl.w_gate, wl.w_up], axis=1), torch.float32), g)
+    c = ops.gemm_fp4_epilogue_none(a, b, out_dtype=torch.bfloat16)
+    h = ops.swiglu(c, g)
+    hq = ops.quantize_mxfp4(h)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, wl.m - 1], np.random.default_rng(6).choice(wl.m, 14, replace=False)]))
+    ac, as_ = mxfp4.quantize(wl.x[rows].astype(np.float64))
+    gc_, gs_ = mxfp4.quantize(wl.w_gate.astype(np.float64).T)
+    uc_, us_ = mxfp4.quantize(wl.w_up.astype(np.float64).T)
+    h_ref = ogemm.swiglu(obf16.round_bf16(ogemm.gemm(ac, as_, gc_, gs_)),
+                         obf16.round_bf16(ogemm.gemm(ac, as_, uc_, us_)))
+    parity.assert_close(host(h)[rows], h_ref, parity.TOL_BF16, what="unfused swiglu chain")
+    codes = layout.untile_codes(host(hq.codes), wl.m, n_half)[rows]
+    scales = layout.untile_scales(host(hq.scales), wl.m, n_half)[rows]
+    # h passed through bf16 three times (gate, up, h), and an fp32 GEMM sum can
+    # round gate or up to the neighbouring bf16 value: |h - h_ref| is within
+    # 2 * 2^-8 + 2^-9 < 2^-6 of |h_ref|, so the band is 2^-6 relative, both
+    # for a code's distance to a rounding midpoint and for a block amax's
+    # distance to a power of two.
+    rel = 2.0 ** -6
+    ref = mxfp4.quantize(h_ref, return_scaled=True)
+    exc, _ = parity.assert_codes_banded(codes, scales, h_ref, "unfused swiglu chain codes", ref=ref,
+                                        tau=np.abs(ref[2]) * rel + parity.TAU, amax_rel=rel)
+    assert exc <= 0.02 * h_ref.size
