@@ -38,6 +38,7 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_MXFP4_TFLOPS = 10100.0     # MI355X dense MXFP4 matrix peak
+PER_LAYER_STEPS = 20       # untimed steps after the timed ones, for every GEMM's duration
 PEAK_CLOCK_GHZ = 2.4            # the clock that peak is quoted at
 PEAK_HBM_GBS = 8000.0
 QUANT_BATCH = 20               # back-to-back launches timed for the quantisation figure
@@ -381,14 +382,16 @@ def main():
     dom = max(range(len(layers)), key=lambda i: layers[i].flops)
     quant_dom = max(range(len(layers)), key=lambda i: layers[i].quant_bytes())
 
-    def step(s, ev=None):
+    def step(s, ev=None, bracket=None):
+        # ev: events around the GEMMs of the layers in `bracket` (default: the dominant one)
         for i, L in enumerate(layers):
             L.quantize(s)
-            if ev is not None and i == dom:
-                ev["g0"][s].record()
+            timed = ev is not None and i in (bracket or (dom,))
+            if timed:
+                ev[(i, 0)][s].record()
             L.gemm()
-            if ev is not None and i == dom:
-                ev["g1"][s].record()
+            if timed:
+                ev[(i, 1)][s].record()
             L.epilogue()
 
     t_warm = time.perf_counter()
@@ -402,7 +405,7 @@ def main():
         step(s)
     torch.cuda.synchronize()
 
-    ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)] for k in ("g0", "g1")}
+    ev = {(dom, k): [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)] for k in (0, 1)}
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -413,6 +416,16 @@ def main():
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # Every layer's GEMM duration, from PER_LAYER_STEPS more steps of the same
+    # mix with events around all of its GEMMs.  Kept out of the timed steps:
+    # each event record puts a few microseconds between kernels (four more
+    # per step cost the step 3.5%).
+    all_layers = tuple(range(len(layers)))
+    ev_all = {(i, k): [torch.cuda.Event(enable_timing=True) for _ in range(PER_LAYER_STEPS)]
+              for i in all_layers for k in (0, 1)}
+    for s in range(PER_LAYER_STEPS):
+        step(s, ev_all, all_layers)
+    torch.cuda.synchronize()
     # the clock under a sustained FP4 MFMA load: right after the timed region,
     # the probe loads every CU with FP4 MFMAs for about a millisecond (the
     # steps' own clock, read inside the GEMM the same way in a timing copy,
@@ -434,7 +447,14 @@ def main():
     flops = sum(L.flops for L in layers)
     tflops = flops / (ms_step * 1e-3) / 1e12
 
-    g_ms = [ev["g0"][s].elapsed_time(ev["g1"][s]) for s in range(args.steps)]
+    g_ms = [ev[(dom, 0)][s].elapsed_time(ev[(dom, 1)][s]) for s in range(args.steps)]
+    per_gemm = []
+    for i, L in enumerate(layers):
+        us = 1e3 * float(np.mean([ev_all[(i, 0)][s].elapsed_time(ev_all[(i, 1)][s])
+                                  for s in range(PER_LAYER_STEPS)]))
+        tf = L.flops / (us * 1e-6) / 1e12
+        per_gemm.append({"layer": L.name, "M": L.m, "N": L.n, "K": L.k, "avg_us": round(us, 2),
+                         "tflops": round(tf, 1), "frac": round(tf / PEAK_MXFP4_TFLOPS, 4)})
     g_avg = float(np.mean(g_ms))
     # The activation-quantisation kernel is ~10 us: a pair of events around a
     # single launch would mostly time the dispatch gap, so after the timed
@@ -507,6 +527,7 @@ def main():
             "avg_launch_ms": round(g_avg, 5),
             "algorithmic_bytes": Ld.gemm_bytes(),
         },
+        "gemms": per_gemm,
         "quantize_roofline": {
             "kernel": ("block_transform" if Lq.t is not None else "quantize_mxfp4") + " (%s, %dx%d bf16)"
                       % (Lq.name, Lq.m, Lq.k),
