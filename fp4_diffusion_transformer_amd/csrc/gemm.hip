@@ -43,6 +43,7 @@
 #include <type_traits>
 
 #include "device_common.hpp"
+#include "gemm_plan.hpp"
 #include "launch.hpp"
 
 namespace fp4dit {
@@ -159,44 +160,10 @@ __device__ __forceinline__ int fresh_lane_id() {
     return (int)l;
 }
 
-// Per-lane byte offsets of the direct-to-LDS loads, fixed for the K loop (the
-// stage advances the wave-uniform base pointers instead).
-struct LoadPlan {
-    uint32_t w_code[4], x_code[4];
-    uint32_t w_scale, x_scale;
-};
-
-// Operands are MX_TILED: K stage kt of rows (2p, 2p+1) is one 128-byte code
-// tile at ((p * K/128) + kt) * 128, and stage kt of 32 rows is one 128-byte
-// scale tile, so every load fetches whole cache lines.
-__device__ __forceinline__ uint32_t code_tile_off(uint32_t r, uint32_t kq) {
-    return ((r >> 1) * kq) * 128 + (r & 1) * 64;
-}
-__device__ __forceinline__ uint32_t scale_tile_off(uint32_t r, uint32_t kq) {
-    return ((r >> 5) * kq) * 128 + (r & 31) * 4;
-}
-
-// Each wave loads 64 of the 256 weight rows and 64 of the 256 token rows:
-// one instruction moves 16 rows x 64 B (lane: row lane/4, 16-byte chunk
-// lane%4, written at its swizzled position), the scale instructions 64 rows
-// x 4 B.
-__device__ __forceinline__ LoadPlan make_plan(int M, int K, int n0, int m0, int wave, int lane) {
-    LoadPlan p;
-    const uint32_t kq = (uint32_t)(K / 128);            // K stages (tiles per row pair / row block)
-    const int rin = lane >> 2;                          // row within a 16-row group
-    const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);  // chunk for physical slot lane & 3
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int row = (wave * 4 + j) * 16 + rin;
-        p.w_code[j] = code_tile_off((uint32_t)(n0 + row), kq) + lchunk * 16;
-        const int xr = m0 + row < M ? m0 + row : M - 1; // ragged token tile: clamp, never stored
-        p.x_code[j] = code_tile_off((uint32_t)xr, kq) + lchunk * 16;
-    }
-    p.w_scale = scale_tile_off((uint32_t)(n0 + wave * 64 + lane), kq);
-    const int xr = m0 + wave * 64 + lane < M ? m0 + wave * 64 + lane : M - 1;
-    p.x_scale = scale_tile_off((uint32_t)xr, kq);
-    return p;
-}
+using plan::LoadPlan;
+using plan::QPlan;
+using plan::make_plan;
+using plan::make_qplan;
 
 // Buffer descriptors of the four operand arrays (scalar registers, set up
 // once): every load of a stage then adds the same scalar offset kt * 128 to
@@ -211,12 +178,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const uint8_t* p, 
 }
 
 __device__ __forceinline__ Operands make_operands(const GemmArgs& g) {
-    const int64_t m2 = (g.M + 1) & ~int64_t(1), m32 = (g.M + 31) & ~int64_t(31);
     Operands o;
-    o.wc = buffer_rsrc(g.b_codes, g.N * (g.K / 2));
-    o.xc = buffer_rsrc(g.a_codes, m2 * (g.K / 2));
-    o.ws = buffer_rsrc(g.b_scales, g.N * (g.K / 32));
-    o.xs = buffer_rsrc(g.a_scales, m32 * (g.K / 32));
+    o.wc = buffer_rsrc(g.b_codes, plan::code_bytes(g.N, g.K));
+    o.xc = buffer_rsrc(g.a_codes, plan::code_bytes(g.M, g.K));
+    o.ws = buffer_rsrc(g.b_scales, plan::scale_bytes(g.N, g.K));
+    o.xs = buffer_rsrc(g.a_scales, plan::scale_bytes(g.M, g.K));
     return o;
 }
 
@@ -473,8 +439,13 @@ __device__ __forceinline__ void k_stage(v16f (&acc)[4][4], Frags& f0, Frags& f1,
 // feature 16s + 8(e/4) + 4h + e%4, and the A operand (lane = output feature
 // r32) is gathered from T_b's rows in the same order.  The result has the
 // accumulator layout again, ready for the requant.  h is fp32 and the MFMA
-// takes bf16, so h is split into hi = bf16(h) and lo = bf16(h - hi) and both
-// parts are multiplied (h - hi - lo is below 2^-16 |h|).
+// takes bf16, so h is carried as three bf16 parts, hi = bf16(h),
+// mid = bf16(h - hi), lo = bf16(h - hi - mid) (each difference is exact in
+// fp32): with RNE each part takes the next 8 significant bits of what is
+// left, so hi + mid + lo equals h exactly for every h whose residuals stay
+// in the normal range (|h| above about 2^-100).  Every bf16 x bf16 product
+// is exact in fp32, so y differs from h_b . T_b only by the order of the
+// fp32 sums.
 __device__ __forceinline__ void load_t_frags(v8s (&tf)[2][2], const GemmArgs& g, int64_t blk0, int r32, int h) {
     // 32-bit element offsets from the scalar base (T is far below 2^31
     // elements), so no per-lane 64-bit address stays live across tiles
@@ -492,22 +463,29 @@ __device__ __forceinline__ void load_t_frags(v8s (&tf)[2][2], const GemmArgs& g,
 }
 
 __device__ __forceinline__ void transform_block(float* hv, const v8s (&tf)[2]) {
-    v8s hi[2], lo[2];
+    v8s hi[2], mid[2], lo[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
             const float a = hv[8 * s + e], b = hv[8 * s + e + 1];
             const uint32_t ph = pack_bf16x2(a, b);
-            const uint32_t pl = pack_bf16x2(a - bf16_bits_to_f32(ph & 0xFFFFu), b - bf16_bits_to_f32(ph >> 16));
+            const float ra = a - bf16_bits_to_f32(ph & 0xFFFFu), rb = b - bf16_bits_to_f32(ph >> 16);
+            const uint32_t pm = pack_bf16x2(ra, rb);
+            const uint32_t pl = pack_bf16x2(ra - bf16_bits_to_f32(pm & 0xFFFFu), rb - bf16_bits_to_f32(pm >> 16));
             hi[s][e] = (short)(ph & 0xFFFFu);
             hi[s][e + 1] = (short)(ph >> 16);
+            mid[s][e] = (short)(pm & 0xFFFFu);
+            mid[s][e + 1] = (short)(pm >> 16);
             lo[s][e] = (short)(pl & 0xFFFFu);
             lo[s][e + 1] = (short)(pl >> 16);
         }
+    // smallest parts first
     v16f y = {};
     y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[0], lo[0], y, 0, 0, 0);
     y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[1], lo[1], y, 0, 0, 0);
+    y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[0], mid[0], y, 0, 0, 0);
+    y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[1], mid[1], y, 0, 0, 0);
     y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[0], hi[0], y, 0, 0, 0);
     y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[1], hi[1], y, 0, 0, 0);
 #pragma unroll
@@ -743,28 +721,6 @@ __device__ __forceinline__ void tile_start_barrier_swiglu(int per_mb) {
 // where the full tiles' schedule would leave three quarters of the CUs idle.
 constexpr int kQDma = 7;
 
-struct QPlan {
-    uint32_t w_code[4], x_code, w_scale, x_scale;
-};
-
-__device__ __forceinline__ QPlan make_qplan(int M, int K, int n0, int m0, int wave, int lane) {
-    QPlan p;
-    const uint32_t kq = (uint32_t)(K / 128);
-    const int rin = lane >> 2;
-    const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        p.w_code[j] = code_tile_off((uint32_t)(n0 + (wave * 4 + j) * 16 + rin), kq) + lchunk * 16;
-    const int xr = m0 + wave * 16 + rin < M ? m0 + wave * 16 + rin : M - 1;
-    p.x_code = code_tile_off((uint32_t)xr, kq) + lchunk * 16;
-    p.w_scale = scale_tile_off((uint32_t)(n0 + wave * 64 + lane), kq);
-    // every wave loads all 64 token-scale rows (identical data to the same
-    // LDS bytes): one unconditional load, no branch inside the K loop
-    const int sr = m0 + lane < M ? m0 + lane : M - 1;
-    p.x_scale = scale_tile_off((uint32_t)sr, kq);
-    return p;
-}
-
 __device__ __forceinline__ void issue_qstage(uint8_t* stage, const Operands& o, const QPlan& p, int kt, int wave,
                                              int lane) {
     const uint32_t soff = (uint32_t)kt * 128u;
@@ -839,23 +795,27 @@ __device__ __forceinline__ void q_mfma(v16f (&acc)[4][1], const QFrags& f) {
 // faster than loads, reads and MFMAs one after the other, and neither
 // removing the weight loads nor making every quarter read the same operands
 // changed that time much.)  Every stage has the same
-// body: near the end of K the loads of stages past the last one still go
-// out (in-bounds buffer loads whose data nobody reads; they land before the
-// epilogue) and the last stage reads a next stage it never uses, so the
-// loop has no branch inside a stage and the barrier count is always one
-// stage of loads.
+// body: near the end of K (and in the prologue when K has fewer than three
+// stages) the loads of stages past the last one still go out, but fetch the
+// last stage again (plan::qload_stage, a scalar min; the buffer loads'
+// scalar offset escapes the hardware's range check, so the stage index
+// itself must stay in range) into a slot nobody reads any more, and the
+// last stage reads a next stage it never uses, so the loop has no branch
+// inside a stage and the barrier count is always one stage of loads.
 template <int EPI, int OUT>
 __device__ __forceinline__ void quarter_tile(const GemmArgs& g, const Operands& ops, uint8_t* const* slots, int n0,
                                              int m0, int wave) {
-    constexpr int D = 3;                               // stages in flight
+    constexpr int D = plan::kQDepth;                   // stages in flight
     const int M = (int)g.M, K = (int)g.K;
     const int kt_count = K / kBK;                      // >= 2
     const int wn = wave & 1, wm = wave >> 1;
     const int lane = fresh_lane_id();
     const int r32 = lane & 31, h = lane >> 5;
-    const QPlan plan = make_qplan(M, K, n0, m0, wave, lane);
+    const QPlan qp = make_qplan(M, K, n0, m0, wave, lane);
     ring_barrier<63>();                                // every wave is done with the ring (last epilogue)
-    static_for<0, D>([&](auto j) { issue_qstage(slots[j()], ops, plan, j(), wave, lane); });
+    static_for<0, D>([&](auto j) {
+        issue_qstage(slots[j()], ops, qp, plan::qload_stage(j(), kt_count), wave, lane);
+    });
     ring_barrier<(D - 1) * kQDma>();                   // stage 0 landed
     v16f acc[4][1];
 #pragma unroll
@@ -883,11 +843,11 @@ __device__ __forceinline__ void quarter_tile(const GemmArgs& g, const Operands& 
                 asm volatile("" : "+s"(zero));
                 const uint8_t* rd = slots[(kS + 1) % 3] + zero;
                 const uint32_t wr = opaque_sgpr(lds_addr(slots[kS % 3]));
-                const uint32_t soff = (uint32_t)(kt + D) * 128u;
+                const uint32_t soff = (uint32_t)plan::qload_stage(kt + D, kt_count) * 128u;
                 static_for<0, 8>([&](auto i) {
                     constexpr int kI = decltype(i)::value;
                     q_mfma<kI>(acc, cur);
-                    if constexpr (kI < 7) issue_qload(kI, wr, ops, plan, soff, wave);
+                    if constexpr (kI < 7) issue_qload(kI, wr, ops, qp, soff, wave);
                     read_qfrag<2 * kI>(nxt, rd, wn, wm, r32, h);
                     if constexpr (2 * kI + 1 < 15) read_qfrag<2 * kI + 1>(nxt, rd, wn, wm, r32, h);
                     __builtin_amdgcn_sched_barrier(0);

@@ -10,11 +10,12 @@
 // Online kernel (HBM-bound): one wave owns 4 consecutive blocks (128
 // channels) of 4 x 32 tokens; each 32-token group is staged in LDS by
 // direct-to-LDS loads of whole rows (double-buffered, see issue_group).  Per
-// block it runs two bf16 MFMAs V_MFMA_F32_32X32X16_BF16 computing
-// Y_b^T = T_b^T . X_b^T, i.e. lane l ends with token l%32 and output
-// features 8a + 4(l/32) + r (a, r = 0..3) -- the same accumulator layout as
-// the GEMM epilogue, so the fused MXFP4 encoding is shared with it: the
-// block amax is one in-lane max plus one lane-swap (v_permlane32_swap).
+// block it runs two bf16 MFMAs V_MFMA_F32_32X32X16_BF16 (six for an fp32 x,
+// carried as three bf16 parts) computing Y_b^T = T_b^T . X_b^T, i.e. lane l
+// ends with token l%32 and output features 8a + 4(l/32) + r (a, r = 0..3) --
+// the same accumulator layout as the GEMM epilogue, so the fused MXFP4
+// encoding is shared with it: the block amax is one in-lane max plus one
+// lane-swap (v_permlane32_swap).
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -139,8 +140,14 @@ __global__ __launch_bounds__(256) void block_transform_kernel(const void* __rest
         for (int j = 0; j < 4; ++j) {
             const int64_t b = b0 + j;
             if (b >= nblk) break;                                   // wave-uniform
-            // B operand: features 16 half + 8h .. +7 of block j for token r32
-            v8s xf[2];
+            // B operand: features 16 half + 8h .. +7 of block j for token r32.
+            // A bf16 x is the operand itself.  An fp32 x is carried as three
+            // bf16 parts hi + mid + lo (hi = bf16(x), mid = bf16(x - hi),
+            // lo = bf16(x - hi - mid); the differences are exact in fp32),
+            // which equal x exactly for |x| above about 2^-100, so y is
+            // formed from the caller's values and only the order of the fp32
+            // sums differs from x_b . T_b.
+            v8s xf[2], xm[2], xl[2];
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int g = 2 * half + h;                         // 8-feature group in the block
@@ -156,18 +163,31 @@ __global__ __launch_bounds__(256) void block_transform_kernel(const void* __rest
                     const int c0 = (8 * j + 2 * g) ^ (r32 & 15), c1 = (8 * j + 2 * g + 1) ^ (r32 & 15);
                     const v4f v0 = *reinterpret_cast<const v4f*>(row + c0 * 16);
                     const v4f v1 = *reinterpret_cast<const v4f*>(row + c1 * 16);
+                    const float xv[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
 #pragma unroll
-                    for (int i = 0; i < 2; ++i) {
-                        const uint32_t p0 = pack_bf16x2(v0[2 * i], v0[2 * i + 1]);
-                        const uint32_t p1 = pack_bf16x2(v1[2 * i], v1[2 * i + 1]);
-                        xf[half][2 * i] = (short)(p0 & 0xFFFFu);
-                        xf[half][2 * i + 1] = (short)(p0 >> 16);
-                        xf[half][4 + 2 * i] = (short)(p1 & 0xFFFFu);
-                        xf[half][4 + 2 * i + 1] = (short)(p1 >> 16);
+                    for (int e = 0; e < 8; e += 2) {
+                        const uint32_t ph = pack_bf16x2(xv[e], xv[e + 1]);
+                        const float ra = xv[e] - bf16_bits_to_f32(ph & 0xFFFFu);
+                        const float rb = xv[e + 1] - bf16_bits_to_f32(ph >> 16);
+                        const uint32_t pm = pack_bf16x2(ra, rb);
+                        const uint32_t pl = pack_bf16x2(ra - bf16_bits_to_f32(pm & 0xFFFFu),
+                                                        rb - bf16_bits_to_f32(pm >> 16));
+                        xf[half][e] = (short)(ph & 0xFFFFu);
+                        xf[half][e + 1] = (short)(ph >> 16);
+                        xm[half][e] = (short)(pm & 0xFFFFu);
+                        xm[half][e + 1] = (short)(pm >> 16);
+                        xl[half][e] = (short)(pl & 0xFFFFu);
+                        xl[half][e + 1] = (short)(pl >> 16);
                     }
                 }
             }
             v16f acc = {};
+            if (!kXBf16) {                                          // smallest parts first
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[j][0], xl[0], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[j][1], xl[1], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[j][0], xm[0], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[j][1], xm[1], acc, 0, 0, 0);
+            }
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[j][0], xf[0], acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[j][1], xf[1], acc, 0, 0, 0);
             float hv[16];

@@ -126,8 +126,12 @@ fp4dit_status fp4dit_quantize_mxfp4(const void* x, fp4dit_dtype x_dtype,
  * codes, scales  both NULL, or both set: MXFP4 of the fp32 product exactly as
  *         fp4dit_quantize_mxfp4 would encode it, in `layout` (x never
  *         round-trips HBM).
- * At least one of y / codes must be set.  Products are formed from bf16
- * operands (an F32 x is rounded to bf16 first) and summed in fp32.
+ * At least one of y / codes must be set.  Products are exact and summed in
+ * fp32: a BF16 x is the matrix-core operand itself; an F32 x is carried as
+ * three bf16 parts (hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi -
+ * mid)) whose sum is x exactly for |x| >= 2^-100 (below that, the part lost
+ * is under 2^-133 in absolute value), so y is formed from the caller's
+ * values and differs from x_b . T_b only by the order of the fp32 sums.
  * Requires cols % 32 == 0.
  */
 fp4dit_status fp4dit_block_transform(const void* x, fp4dit_dtype x_dtype,
@@ -250,9 +254,9 @@ fp4dit_status fp4dit_gemm_fp4_epilogue_swiglu(int64_t M, int64_t N, int64_t K,
  * block before it is quantised).  With h [M][N/2] as in
  * fp4dit_gemm_fp4_epilogue_swiglu (same B packing and constraints on N):
  *     y[m][32b + j] = sum_i h[m][32b + i] * T_b[i][j]
- * computed from the fp32 h (not a bf16 copy of it; the product is formed
- * from bf16 parts h = hi + lo with fp32 accumulation, so its error is below
- * 2^-16 of sum_i |h_i T_b[i][j]|), then MXFP4-quantised along its columns.
+ * computed from the fp32 h (not a bf16 copy of it: h is carried exactly as
+ * three bf16 parts, as an F32 x in fp4dit_block_transform, and the products
+ * are summed in fp32), then MXFP4-quantised along its columns.
  * t_bf16     [n_t][32][32] bfloat16 bit patterns, row i = input feature,
  *            2-byte aligned; n_t = 1 (one T for every block) or N/64.
  * y          NULL, or [M][N/2] of y_dtype (16-byte aligned): y itself.

@@ -44,8 +44,22 @@ def rel_err(gpu, ref, group=None):
     return float(np.max(np.abs(g - r) / denom))
 
 
-def assert_close(gpu, ref, tol, group=None, what=""):
-    e = rel_err(gpu, ref, group)
+def assert_close(gpu, ref, tol, group=None, what="", mask=None):
+    """rel_err over all elements, or over those where `mask` is set (the
+    RMS floor still comes from the whole row or head of the reference)."""
+    if mask is None:
+        e = rel_err(gpu, ref, group)
+    else:
+        g = np.asarray(gpu, dtype=np.float64)
+        r = np.asarray(ref, dtype=np.float64)
+        m, n = r.shape
+        grp = n if group is None else group
+        rr = r.reshape(m, n // grp, grp)
+        rms = np.sqrt(np.mean(rr * rr, axis=2, keepdims=True))
+        denom = np.maximum(np.abs(r), np.broadcast_to(0.1 * rms, rr.shape).reshape(m, n))
+        denom = np.where(denom == 0, 1.0, denom)
+        err = np.abs(g - r) / denom
+        e = float(np.max(err[mask])) if np.any(mask) else 0.0
     assert e <= tol, "%s: max relative error %.3e > %.1e" % (what, e, tol)
     return e
 
@@ -71,26 +85,6 @@ def _near_midpoint(q, tau=TAU):
     for mid in mxfp4.E2M1_MIDPOINTS:
         near |= np.abs(a - mid) <= tau
     return near
-
-
-def split_product_bands(h, t, ref_scales):
-    """Bands for codes of y = h . T formed on the GPU from bf16 parts
-    h = hi + lo of an fp32 h: the neglected h - hi - lo is below 2^-16 |h|,
-    so |y_gpu - y| <= 2^-16 mag with mag_o = sum_i |h_i T_io|, on top of the
-    fp32 error that TAU and AMAX_REL cover.  h, t: the oracle's float64 h
-    and T.  Returns (tau per element in scaled units, amax_rel per block)."""
-    h = np.abs(np.asarray(h, dtype=np.float64))
-    t = np.abs(np.asarray(t, dtype=np.float64))
-    m, n = h.shape
-    mag = np.empty_like(h)
-    for b in range(n // 32):
-        mag[:, 32 * b:32 * b + 32] = h[:, 32 * b:32 * b + 32] @ (t[0] if t.shape[0] == 1 else t[b])
-    shared = np.repeat(np.asarray(ref_scales, dtype=np.float64) - 127.0, 32, axis=1)
-    tau = TAU + 2.0 ** -16 * mag / 2.0 ** shared
-    # amax >= 2^(shared + 2) for every block with a nonzero amax
-    blk_mag = np.max(mag.reshape(m, n // 32, 32), axis=2)
-    amax_rel = AMAX_REL + 2.0 ** -16 * blk_mag / 2.0 ** (np.asarray(ref_scales, dtype=np.float64) - 125.0)
-    return tau, amax_rel
 
 
 def _near_pow2(amax, amax_rel=AMAX_REL):
@@ -128,13 +122,14 @@ def assert_codes_banded(gpu_packed, gpu_scales, ref_values, what="", ref=None, t
 def assert_fused_codes(gpu_codes, gpu_scales, c_gate, c_up, t, what=""):
     """Unpacked-row codes / scales of the fused SwiGLU -> block transform ->
     MXFP4 epilogue against the oracle's, from the oracle's accumulators
-    c_gate, c_up (float64) and T, with the split-product bands.  Returns
-    (h, y_ref, excused codes, excused blocks)."""
+    c_gate, c_up (float64) and T, with the plain midpoint band (the kernel
+    carries the fp32 h exactly, as three bf16 parts, so only the order of
+    its fp32 sums differs).  Returns (h, y_ref, excused codes, excused
+    blocks)."""
     t64 = np.asarray(t, dtype=np.float64)
     rc, rs, q = ogemm.swiglu_transform_requantize(c_gate, c_up, t64, return_scaled=True)
     h = ogemm.swiglu(c_gate, c_up)
     y_ref = otransform.block_transform(h, t64)
-    tau, amax_rel = split_product_bands(h, t64, rs)
-    exc, blk = assert_codes_banded(gpu_codes, gpu_scales, y_ref, what, ref=(rc, rs, q), tau=tau, amax_rel=amax_rel)
-    assert exc <= 0.002 * y_ref.size and blk <= 0.002 * rs.size, "%s: %d codes / %d blocks excused" % (what, exc, blk)
+    exc, blk = assert_codes_banded(gpu_codes, gpu_scales, y_ref, what, ref=(rc, rs, q))
+    assert exc <= 0.001 * y_ref.size and blk <= 0.001 * rs.size, "%s: %d codes / %d blocks excused" % (what, exc, blk)
     return h, y_ref, exc, blk

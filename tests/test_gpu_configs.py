@@ -221,3 +221,142 @@ def test_dit_block_up_fused_down_transform():
     torch.cuda.synchronize()
     codes, scales = _untile(mx)
     parity.assert_fused_codes(codes[rows], scales[rows], c_g, c_u, down.t, "dit up fused down transform")
+
+
+# ----------------------------------------------------------------------------
+# The batch-4 block chained on the GPU exactly as the benchmark runs it.
+
+def _gpu_weight(w, t_dev, group):
+    """The benchmark's weight preparation on the GPU: fold T^-1, pack (tiled)."""
+    return ops.pack_weight(ops.fold_inverse_transform(dev(w, torch.float32), t_dev), interleave_group=group)
+
+
+def _oracle_weight_codes(w, t64, src):
+    """Oracle codes of the folded weight in physical column order [N, K]."""
+    w_fold = transform.fold_inverse(w.astype(np.float64), t64)[:, src]
+    return mxfp4.quantize(w_fold.T)
+
+
+def _equal_rows(gpu_mx, ref_codes, ref_scales, rows):
+    """Rows (of `rows`) whose GPU codes and scales equal the oracle's."""
+    gc, gs = _untile(gpu_mx)
+    gc, gs = gc[rows], gs[rows]
+    return np.all(gc == mxfp4.pack_codes(ref_codes), axis=1) & np.all(gs == ref_scales, axis=1)
+
+
+def _equal_weight_rows(gpu_mx, bc, bs):
+    """Physical output columns whose GPU weight codes and scales (all of K)
+    equal the oracle's."""
+    gc, gs = _untile(gpu_mx)
+    return np.all(gc == mxfp4.pack_codes(bc), axis=1) & np.all(gs == bs, axis=1)
+
+
+@pytest.mark.parametrize("stage", ["qkv", "up", "down"])
+def test_dit_block_batch4_chain(stage):
+    """Each stage of the batch-4 block chained on the GPU as the benchmark
+    runs it -- block transform + quantise of the activations, T^-1 folded
+    into the weight and packed, fused GEMM + epilogue, all on the device --
+    against the oracle run from the same inputs (x, W, T, gains) on sampled
+    rows.  The transform and the fold are fp32 sums on the GPU, so a code on
+    a rounding midpoint may differ (within the S13 band, checked by the stage
+    test above); where one does, the whole row (activations) or output
+    column (weights) legitimately differs, so those are left out and
+    counted, and everything else must meet the plain tolerance."""
+    wl = dict(zip(["qkv", "up", "down"], _dit_block()))[stage]
+    t64 = wl.t.astype(np.float64)
+    announce("config dit_block chain", stage, wl.m, wl.n, wl.k)
+    t_dev = dev(wl.t, torch.bfloat16)
+    _, a = ops.block_transform(dev(wl.x, torch.bfloat16), t_dev, quantize=True)
+    if wl.epilogue == "swiglu":
+        w = np.concatenate([wl.w_gate, wl.w_up], axis=1)
+        group = ops.swiglu_interleave_group()
+        pair, is_up = ogemm.interleave_columns(wl.w_gate.shape[1], group)
+        src = np.where(is_up, pair + wl.w_gate.shape[1], pair)
+    else:
+        w, group, src = wl.w, 0, np.arange(wl.w.shape[1])
+    b = _gpu_weight(w, t_dev, group)
+    if stage == "qkv":
+        out = ops.gemm_fp4_epilogue_rmsnorm_head(a, b, wl.head_dim, wl.n_norm, dev(wl.norm_w, torch.float32),
+                                                 wl.eps)
+    elif stage == "up":
+        out, _ = ops.gemm_fp4_epilogue_swiglu(a, b, out_dtype=torch.bfloat16)
+    else:
+        out = ops.gemm_fp4_epilogue_none(a, b)
+    torch.cuda.synchronize()
+    rows = _rows(wl.m, n=24, seed=11)
+    ac, as_ = transform.transform_quantize(wl.x[rows].astype(np.float64), t64)
+    keep_r = _equal_rows(a, ac, as_, rows)
+    bc, bs = _oracle_weight_codes(w, t64, src)
+    keep_c = _equal_weight_rows(b, bc, bs)                        # per physical column
+    c = ogemm.gemm(ac[keep_r], as_[keep_r], bc, bs)
+    got = host(out)[rows[keep_r]]
+    if stage == "qkv":
+        ref = ogemm.rmsnorm_head(c, wl.head_dim, wl.n_norm, wl.norm_w.astype(np.float64), wl.eps)
+        # a normalised head depends on all of its columns
+        heads = keep_c[:wl.n_norm].reshape(-1, wl.head_dim).all(axis=1)
+        col_ok = np.concatenate([np.repeat(heads, wl.head_dim), keep_c[wl.n_norm:]])
+        group_cols = wl.head_dim
+    elif stage == "up":
+        ref = ogemm.swiglu_from_interleaved(c, group)
+        # output j comes from its gate and its up column
+        n_half = wl.w_gate.shape[1]
+        ok_logical = np.zeros(2 * n_half, dtype=bool)
+        ok_logical[src] = keep_c
+        col_ok = ok_logical[:n_half] & ok_logical[n_half:]
+        group_cols = None
+    else:
+        ref, col_ok, group_cols = c, keep_c, None
+    n_rows, n_cols = int(keep_r.sum()), int(col_ok.sum())
+    print("[chain %s] rows compared %d of %d (%d left out: an activation code on a midpoint); output columns "
+          "compared %d of %d (%d left out: a folded-weight code on a midpoint)"
+          % (stage, n_rows, len(rows), len(rows) - n_rows, n_cols, col_ok.size, col_ok.size - n_cols), flush=True)
+    assert n_rows >= len(rows) // 2 and n_cols >= 0.9 * col_ok.size, "too many codes on midpoints"
+    mask = np.broadcast_to(col_ok, ref.shape)
+    parity.assert_close(got, ref, parity.TOL_BF16, group=group_cols, what="dit chain " + stage, mask=mask)
+
+
+def test_dit_block_batch4_fused_chain():
+    """The benchmark's fused batch-4 block from the FFN-up input to the down
+    projection's output, entirely on the GPU: up-input transform + quantise,
+    FFN-up GEMM with SwiGLU -> the down layer's 384 block transforms -> MXFP4
+    in its epilogue, then the down GEMM (weights folded and packed on the
+    GPU) -- against the oracle's SwiGLU -> transform -> quantise -> down GEMM
+    from the same inputs.  Rows are compared where the GPU's up activations
+    and its fused down activations both equal the oracle's codes (else a code
+    on a midpoint changed the row; counted), and output columns where the
+    down weight codes equal the oracle's."""
+    _, up, down = _dit_block()
+    t_up, t_dn = up.t.astype(np.float64), down.t.astype(np.float64)
+    announce("config dit_block fused chain", up.m, up.n, up.k, down.n)
+    _, a_up = ops.block_transform(dev(up.x, torch.bfloat16), dev(up.t, torch.bfloat16), quantize=True)
+    group = ops.swiglu_interleave_group()
+    w_up = np.concatenate([up.w_gate, up.w_up], axis=1)
+    b_up = _gpu_weight(w_up, dev(up.t, torch.bfloat16), group)
+    _, a_dn = ops.gemm_fp4_epilogue_swiglu_transform(a_up, b_up, dev(down.t, torch.bfloat16))
+    b_dn = _gpu_weight(down.w, dev(down.t, torch.bfloat16), 0)
+    out = ops.gemm_fp4_epilogue_none(a_dn, b_dn)
+    torch.cuda.synchronize()
+    del b_up
+    rows = _rows(up.m, n=24, seed=13)
+    ac, as_ = transform.transform_quantize(up.x[rows].astype(np.float64), t_up)
+    keep_up = _equal_rows(a_up, ac, as_, rows)
+    wg = transform.fold_inverse(up.w_gate.astype(np.float64), t_up)
+    wu = transform.fold_inverse(up.w_up.astype(np.float64), t_up)
+    gc_, gs_ = mxfp4.quantize(wg.T)
+    uc_, us_ = mxfp4.quantize(wu.T)
+    del wg, wu
+    c_g = ogemm.gemm(ac, as_, gc_, gs_)
+    c_u = ogemm.gemm(ac, as_, uc_, us_)
+    dc, ds = ogemm.swiglu_transform_requantize(c_g, c_u, t_dn)
+    keep_dn = _equal_rows(a_dn, dc, ds, rows)
+    keep_r = keep_up & keep_dn
+    bc, bs = _oracle_weight_codes(down.w, t_dn, np.arange(down.w.shape[1]))
+    keep_c = _equal_weight_rows(b_dn, bc, bs)
+    ref = ogemm.gemm(dc[keep_r], ds[keep_r], bc, bs)
+    got = host(out)[rows[keep_r]]
+    n_rows, n_cols = int(keep_r.sum()), int(keep_c.sum())
+    print("[fused chain] rows compared %d of %d (up activations differ in %d, fused down activations in %d); "
+          "output columns compared %d of %d" % (n_rows, len(rows), int((~keep_up).sum()), int((~keep_dn).sum()),
+                                                 n_cols, keep_c.size), flush=True)
+    assert n_rows >= len(rows) // 2 and n_cols >= 0.9 * keep_c.size, "too many codes on midpoints"
+    parity.assert_close(got, ref, parity.TOL_BF16, what="dit fused chain", mask=np.broadcast_to(keep_c, ref.shape))

@@ -244,10 +244,13 @@ def _check_fused(mx, y, c_g, c_u, t, rows=None, what="fused"):
     if y is not None:
         yg = host(y)[rows].astype(np.float64)
         parity.assert_close(yg, y_ref, parity.TOL_F32, what=what + " y")
-        # the split-product error bound itself, with slack for fp32 sums
+        # y from the fp32 h carried exactly: besides h's own fp32 error (from
+        # the GEMM's sums and the SiLU, a few 2^-24 relative), only the fp32
+        # summation order; a bf16-rounded h (error up to 2^-9 |h|) or a
+        # two-part split (up to 2^-16 |h|) can exceed this
         mag = otransform.block_transform(np.abs(h_rows), np.abs(t.astype(np.float64)))
         rms = np.sqrt(np.mean(y_ref ** 2, axis=1, keepdims=True))
-        assert np.all(np.abs(yg - y_ref) <= 2.0 ** -16 * mag + 1e-5 * rms), what + ": y outside the bound"
+        assert np.all(np.abs(yg - y_ref) <= 2.0 ** -18 * mag + 1e-5 * rms), what + ": y outside the bound"
 
 
 @pytest.mark.parametrize("m,n_t", [(300, 8), (300, 1), (1, 8)])

@@ -32,11 +32,12 @@ def test_transform_values(rows, cols, n_t, lay, x_dtype):
     rng = np.random.default_rng(rows + cols + n_t)
     x = rng.standard_normal((rows, cols)).astype(np.float32)
     x[:, rng.choice(cols, 2, replace=False)] *= 20
-    xb = workloads.to_bf16_values(x)               # the kernel multiplies bf16 operands
+    # the caller's own values: bf16 for a bf16 x, the full fp32 values for an
+    # fp32 x (which the kernel carries as three bf16 parts)
+    xin = workloads.to_bf16_values(x) if x_dtype == torch.bfloat16 else x
     t = _t(n_t, 40 + n_t)
-    ref = transform.block_transform(xb.astype(np.float64), t.astype(np.float64))
+    ref = transform.block_transform(xin.astype(np.float64), t.astype(np.float64))
     announce("block_transform values", rows, cols, n_t, x_dtype)
-    xin = xb if x_dtype == torch.bfloat16 else x
     y, mx = ops.block_transform(dev(xin, x_dtype), dev(t, torch.bfloat16), y_dtype=torch.float32, quantize=True,
                                 layout=lay)
     parity.assert_close(host(y), ref, 1e-5, what="transform fp32 y")
