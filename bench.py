@@ -60,6 +60,9 @@ def parse():
                                                                  "dit_block_fused"])
     p.add_argument("--rotate", type=int, default=4, help="activation buffer copies cycled over steps")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra-configs", action="store_true",
+                   help="skip the tiny and batch-4 block records that follow the headline workload")
+    p.add_argument("--extra-steps", type=int, default=30, help="timed steps of each batch-4 block record")
     p.add_argument("--calib-mib", type=int, default=0,
                    help="before warm-up, fill a buffer of this many MiB once and then sum it, so that HBM "
                         "write and read counters can be calibrated against kernels of known traffic")
@@ -75,7 +78,7 @@ class Layer:
         dev = "cuda"
         self.m, self.k = wl.m, wl.k
         x = wl.x if x_override is None else x_override
-        xs = [torch.from_numpy(x).to(dev, torch.bfloat16)]
+        xs = [torch.from_numpy(x).to(dev, torch.bfloat16 if wl.x_bf16 else torch.float32)]
         for r in range(1, rotate):                     # distinct copies defeat the LLC
             xs.append(xs[0].clone())
         self.xs = xs
@@ -164,7 +167,7 @@ class Layer:
         """Algorithmic HBM bytes of the activation quantiser: bf16 in, codes + scales out."""
         if self.xs is None:
             return 0
-        return self.m * self.k * 2 + self.m * self.k // 2 + self.m * self.k // 32
+        return self.m * self.k * (2 if self.wl.x_bf16 else 4) + self.m * self.k // 2 + self.m * self.k // 32
 
     def gemm_bytes(self):
         """Algorithmic HBM bytes of the fused GEMM: both MXFP4 operands once, output once."""
@@ -287,8 +290,15 @@ def cpu_baseline(args, layers_wl, rows=2048, min_seconds=10.0, max_windows=8):
             elapsed += time.perf_counter() - t1
             flops += 2 * x.shape[0] * n * wl.k
         windows += 1
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "blas_threads": int(threads), "cpu_count": os.cpu_count(),
+            "sched_affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": model,
             "sample": "%d windows of %d tokens of each layer of the workload (%s); %.1f s timed" % (
                 windows, rows, ", ".join(w.name for w in layers_wl), elapsed)}
 
@@ -356,6 +366,140 @@ def aux_kernels(torch, ops, workloads):
     return out
 
 
+def measure_steps(torch, layers, steps, warmup, warm_seconds, per_layer_steps=PER_LAYER_STEPS):
+    """ms per step of `layers` (each step: every layer's quantise, GEMM and
+    unfused epilogue, if any) over `steps` timed steps after warm-up, and
+    every layer's GEMM duration from per_layer_steps more steps with events
+    around each GEMM."""
+    def step(s, ev=None):
+        for i, L in enumerate(layers):
+            L.quantize(s)
+            if ev is not None:
+                ev[(i, 0)][s].record()
+            L.gemm()
+            if ev is not None:
+                ev[(i, 1)][s].record()
+            L.epilogue()
+
+    t_warm = time.perf_counter()
+    s = 0
+    while time.perf_counter() - t_warm < warm_seconds:
+        step(s)
+        s += 1
+        if s % 20 == 0:
+            torch.cuda.synchronize()
+    for s in range(warmup):
+        step(s)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for s in range(steps):
+        step(s)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / steps
+    ev = {(i, k): [torch.cuda.Event(enable_timing=True) for _ in range(per_layer_steps)]
+          for i in range(len(layers)) for k in (0, 1)}
+    for s in range(per_layer_steps):
+        step(s, ev)
+    torch.cuda.synchronize()
+    gemms = []
+    for i, L in enumerate(layers):
+        us = 1e3 * float(np.mean([ev[(i, 0)][s].elapsed_time(ev[(i, 1)][s]) for s in range(per_layer_steps)]))
+        tf = L.flops / (us * 1e-6) / 1e12
+        gemms.append({"layer": L.name, "M": L.m, "N": L.n, "K": L.k, "avg_us": round(us, 2),
+                      "tflops": round(tf, 1), "frac": round(tf / PEAK_MXFP4_TFLOPS, 4)})
+    return ms_step, gemms
+
+
+def transform_record(torch, L):
+    """GB/s of the layer's block transform + quantise, over enough input
+    copies that every launch reads HBM, as one graph replay."""
+    sets = [L.xs[0].clone() for _ in range(n_sets(L.quant_bytes()))]
+    saved = L.xs
+    L.xs = sets
+    ms = time_rotating(torch, [lambda i=i: L.quantize(i) for i in range(len(sets))])
+    L.xs = saved
+    del sets
+    return hbm_record("block_transform + quantise (%s, %dx%d bf16, %d matrices)" % (L.name, L.m, L.k, L.k // 32),
+                      L.quant_bytes(), ms, "%d launches over %d input copies, one graph replay"
+                      % (QUANT_BATCH, n_sets(L.quant_bytes())))
+
+
+def block_record(ms_step, layers, gemms, workload):
+    flops = sum(L.flops for L in layers)
+    tf = flops / (ms_step * 1e-3) / 1e12
+    return {"workload": workload, "ms_per_step": round(ms_step, 5), "tflops": round(tf, 2),
+            "pct_of_mxfp4_peak": round(100.0 * tf / PEAK_MXFP4_TFLOPS, 2),
+            "layers": [{"name": L.name, "M": L.m, "N": L.n, "K": L.k,
+                        "input": "block transform + quantise" if L.xs is not None
+                        else "MXFP4 from the previous layer's epilogue",
+                        "epilogue": L.wl.epilogue + ("+down_transform+requant" if L.next_t is not None else "")}
+                       for L in layers],
+            "gemms": gemms}
+
+
+def extra_configs(args, torch, ops, workloads):
+    """The other configurations, timed in the same run after the headline:
+    the tiny 256x512x512 case (latency; launch-bound) and the batch-4 DiT
+    block (16384 tokens, block transform on every input), unfused and with
+    the FFN-up epilogue producing the down projection's MXFP4 input."""
+    out = {}
+    # tiny: fp32 X [256, 512] -> quantise -> GEMM + RMSNorm hd 128 (4 heads)
+    wl = workloads.tiny()
+    L = Layer("tiny", wl, ops, torch, 1)
+
+    def tiny_step(s=0):
+        L.quantize(0)
+        L.gemm()
+
+    for _ in range(50):
+        tiny_step()
+    torch.cuda.synchronize()
+    n = 200
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        tiny_step()
+    e1.record()
+    torch.cuda.synchronize()
+    eager_us = e0.elapsed_time(e1) * 1e3 / n
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(n):
+            tiny_step()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_us = e0.elapsed_time(e1) * 1e3 / n
+    out["tiny"] = {"workload": "tiny: X fp32 [256, 512] -> MXFP4 -> GEMM 256x512x512 + RMSNorm hd 128 (4 heads), "
+                               "bf16 out", "us_per_step_eager": round(eager_us, 2),
+                   "us_per_step_graph": round(graph_us, 2),
+                   "tflops_graph": round(L.flops / (graph_us * 1e-6) / 1e12, 2),
+                   "measured": "%d back-to-back steps (quantise + GEMM), events around them; eager launches, "
+                               "then the same steps as one HIP-graph replay" % n,
+                   "bound": "launch / latency (0.134 GFLOP)"}
+    del L, graph
+    # the batch-4 block, unfused then fused; the weights are prepared once
+    bargs = argparse.Namespace(**vars(args))
+    bargs.workload = "dit_block"
+    layers = build_layers(bargs, ops, torch, workloads)
+    ms, gemms = measure_steps(torch, layers, args.extra_steps, 5, 0.3)
+    rec = block_record(ms, layers, gemms, "dit_block")
+    rec["block_transform"] = transform_record(torch, layers[2])
+    out["dit_block"] = rec
+    up, dl = layers[1], layers[2]
+    up.out, up.next_t, up.next_a = None, dl.t, dl.a
+    dl.xs = None
+    ms, gemms = measure_steps(torch, layers, args.extra_steps, 5, 0.3)
+    out["dit_block_fused"] = block_record(ms, layers, gemms, "dit_block_fused")
+    del layers
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -364,10 +508,10 @@ def main():
         sys.exit(2)
     import torch
     sys.path.insert(0, ROOT)
-    from fp4_diffusion_transformer_amd import ops, workloads
+    from fp4_diffusion_transformer_amd import clockprobe, ops, workloads
 
     torch.cuda.init()
-    clk_idle = ops.shader_clock_ghz(1, 64)   # one workgroup, before any load (the shader-clock probe)
+    clk_idle = clockprobe.shader_clock_ghz(1, 64)   # one workgroup, before any load (the shader-clock probe)
     if args.calib_mib:
         buf = torch.empty(args.calib_mib << 18, dtype=torch.float32, device="cuda")
         buf.fill_(1.0)                       # writes calib_mib MiB
@@ -436,10 +580,10 @@ def main():
     p_iters = 3000
     pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     pe0.record()
-    ops.clock_probe(probe, cus, p_iters)
+    clockprobe.clock_probe(probe, cus, p_iters)
     pe1.record()
     torch.cuda.synchronize()
-    clk_load = float(np.median(ops.clock_ghz(probe, cus)))
+    clk_load = float(np.median(clockprobe.clock_ghz(probe, cus)))
     mfma_pf = 2.0 * 32 * 32 * 64 * 16 * p_iters * 4 * cus / (pe0.elapsed_time(pe1) * 1e-3) / 1e15
     del probe
     ms_total = start.elapsed_time(stop)
@@ -559,8 +703,13 @@ def main():
                          "achieved_GBs": round(L.epilogue_bytes() / (ms * 1e-3) / 1e9, 1),
                          "algorithmic_bytes": L.epilogue_bytes()})
         out["unfused_epilogues"] = epis
+    layer_wls = [L.wl for L in layers]
+    if args.workload == "dit_1k_linears" and not args.no_extra_configs:
+        del layers, Lq, Ld
+        torch.cuda.empty_cache()
+        out["configs"] = extra_configs(args, torch, ops, workloads)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args, [L.wl for L in layers])
+        out["cpu_baseline"] = cpu_baseline(args, layer_wls)
     print(json.dumps(out), flush=True)
 
 

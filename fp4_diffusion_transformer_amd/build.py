@@ -48,8 +48,28 @@ def build(verbose=True):
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)
+    build_clock_probe(verbose)
     build_c_consumer(verbose)
     return LIB
+
+
+CLOCK_SRC = os.path.join(HERE, "clockprobe", "clock_probe.hip")
+CLOCK_LIB = os.path.join(HERE, "libfp4dit_clock.so")
+
+
+def build_clock_probe(verbose=True):
+    """The shader-clock probe, a measurement helper, as a library of its own
+    (libfp4dit_clock.so) so that libfp4dit.so holds only the method."""
+    tmp = CLOCK_LIB + ".tmp"
+    cmd = [HIPCC] + [f for f in FLAGS if not f.startswith("-I")] + [
+        "-I" + os.path.dirname(CLOCK_SRC), "-shared", CLOCK_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed on the clock probe:\n" + r.stderr)
+    os.replace(tmp, CLOCK_LIB)
+    if verbose:
+        print("built", CLOCK_LIB)
+    return CLOCK_LIB
 
 
 C_CONSUMER_SRC = os.path.join(ROOT, "tests", "c_consumer.c")

@@ -1,4 +1,5 @@
-// Shader-clock probe, a measurement helper and no step of the method.
+// Shader-clock probe (libfp4dit_clock.so), a measurement helper and no step
+// of the method, built apart from libfp4dit.so.
 //
 // The MXFP4 roofline is quoted at the published 2.4 GHz, but under a
 // sustained FP4 MFMA load the shader clock settles lower (power).  Each wave
@@ -9,13 +10,15 @@
 // the clock that wave ran at.  One workgroup per CU loads the whole chip
 // the way the persistent GEMM does; a single workgroup reads the clock of a
 // lightly loaded chip.
-#include "device_common.hpp"
-#include "launch.hpp"
+#include <hip/hip_runtime.h>
+#include <stdint.h>
 
-namespace fp4dit {
+#include "fp4dit_clock.h"
+
 namespace {
 
 typedef int v8i_ __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ uint32_t mix32(uint32_t x) {        // an integer hash (operand bits)
     x ^= x >> 16;
@@ -71,9 +74,10 @@ __global__ __launch_bounds__(256, 1) void clock_probe_kernel(uint64_t* __restric
 
 }  // namespace
 
-hipError_t launch_clock_probe(uint64_t* out, int workgroups, int iters, hipStream_t stream) {
+extern "C" int32_t fp4dit_clock_probe(uint64_t* out, int32_t workgroups, int32_t iters, hipStream_t stream) {
+    if (!out) return 1;
+    if (reinterpret_cast<uintptr_t>(out) % 8 != 0) return 3;
+    if (workgroups < 1 || workgroups > 65536 || iters < 1 || iters > (1 << 20)) return 2;
     hipLaunchKernelGGL(clock_probe_kernel, dim3(workgroups), dim3(256), 0, stream, out, iters);
-    return hipGetLastError();
+    return hipGetLastError() == hipSuccess ? 0 : 5;
 }
-
-}  // namespace fp4dit

@@ -11,6 +11,7 @@
 
 namespace {
 
+using fp4dit::kGemmKMin;
 using fp4dit::kGemmKMultiple;
 using fp4dit::kGemmNMultiple;
 
@@ -47,7 +48,7 @@ bool requant_fits(int64_t M, int64_t N) {
 fp4dit_status check_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
                          const uint8_t* bc, const uint8_t* bs) {
     if (M < 0 || N <= 0 || K <= 0 || !dims_ok({M, N, K})) return FP4DIT_E_SHAPE;
-    if (N % kGemmNMultiple != 0 || K % kGemmKMultiple != 0) return FP4DIT_E_SHAPE;
+    if (N % kGemmNMultiple != 0 || K % kGemmKMultiple != 0 || K < kGemmKMin) return FP4DIT_E_SHAPE;
     if ((M + 1) * (K / 2) > kMaxOperandBytes || N * (K / 2) > kMaxOperandBytes) return FP4DIT_E_SHAPE;
     if (M == 0) return FP4DIT_OK;
     if (!ac || !as || !bc || !bs) return FP4DIT_E_NULL;
@@ -116,6 +117,31 @@ fp4dit_status fp4dit_fold_inverse_transform(const float* w, int64_t K, int64_t N
     if (w == w_out) return FP4DIT_E_UNSUPPORTED;
     if (!aligned(w, 4) || !aligned(w_out, 4) || !aligned(t_bf16, 2)) return FP4DIT_E_ALIGN;
     return launched(fp4dit::launch_fold_inverse(w, K, N, t_bf16, n_t, w_out, stream));
+}
+
+fp4dit_status fp4dit_mx_relayout(const uint8_t* in_codes, const uint8_t* in_scales, fp4dit_layout in_layout,
+                                 int64_t rows, int64_t cols, uint8_t* out_codes, uint8_t* out_scales,
+                                 fp4dit_layout out_layout, hipStream_t stream) {
+    if (!valid_layout(in_layout) || !valid_layout(out_layout)) return FP4DIT_E_UNSUPPORTED;
+    const bool tiled = in_layout == FP4DIT_MX_TILED || out_layout == FP4DIT_MX_TILED;
+    if (rows < 0 || cols < 0 || cols % (tiled ? 128 : 32) != 0 || !dims_ok({rows, cols})) return FP4DIT_E_SHAPE;
+    if (rows == 0 || cols == 0) return FP4DIT_OK;
+    if (!in_codes || !in_scales || !out_codes || !out_scales) return FP4DIT_E_NULL;
+    if (!aligned(in_codes, 16) || !aligned(out_codes, 16)) return FP4DIT_E_ALIGN;
+    auto code_bytes = [&](fp4dit_layout l) { return (l == FP4DIT_MX_TILED ? (rows + 1) / 2 * 2 : rows) * (cols / 2); };
+    auto scale_bytes = [&](fp4dit_layout l) {
+        return (l == FP4DIT_MX_TILED ? (rows + 31) / 32 * 32 : rows) * (cols / 32);
+    };
+    const void* ins[2] = {in_codes, in_scales};
+    const int64_t in_b[2] = {code_bytes(in_layout), scale_bytes(in_layout)};
+    const void* outs[2] = {out_codes, out_scales};
+    const int64_t out_b[2] = {code_bytes(out_layout), scale_bytes(out_layout)};
+    for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 2; ++j)
+            if (outs[i] == ins[j] || overlaps(outs[i], out_b[i], ins[j], in_b[j])) return FP4DIT_E_UNSUPPORTED;
+    if (outs[0] == outs[1] || overlaps(outs[0], out_b[0], outs[1], out_b[1])) return FP4DIT_E_UNSUPPORTED;
+    return launched(fp4dit::launch_relayout(in_codes, in_scales, in_layout == FP4DIT_MX_TILED, rows, cols, out_codes,
+                                            out_scales, out_layout == FP4DIT_MX_TILED, stream));
 }
 
 fp4dit_status fp4dit_pack_weight(const void* w, fp4dit_dtype w_dtype, int64_t K, int64_t N,
@@ -311,13 +337,6 @@ fp4dit_status fp4dit_etd_coefficients(double alpha_s, double sigma_s, double alp
         *c1 = 0.25 * coeff;
     }
     return FP4DIT_OK;
-}
-
-fp4dit_status fp4dit_clock_probe(uint64_t* out, int32_t workgroups, int32_t iters, hipStream_t stream) {
-    if (!out) return FP4DIT_E_NULL;
-    if (reinterpret_cast<uintptr_t>(out) % 8 != 0) return FP4DIT_E_ALIGN;
-    if (workgroups < 1 || workgroups > 65536 || iters < 1 || iters > (1 << 20)) return FP4DIT_E_SHAPE;
-    return launched(fp4dit::launch_clock_probe(out, workgroups, iters, stream));
 }
 
 }  // extern "C"

@@ -880,7 +880,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
     const int tiles_n = (int)(g.N / kBN);
     const int tiles_m = (M + kBM - 1) / kBM;
     const int n_tiles = tiles_n * tiles_m;
-    const int kt_count = K / kBK;            // even, >= NS - 1 (chosen by the host)
+    const int kt_count = K / kBK;            // >= NS - 1 (the host requires K >= 256)
     const Operands ops = make_operands(g);
 
     // Stage j lives in ring slot (j + OFF) % NS.  The first PEEL stages run
@@ -1027,7 +1027,7 @@ void launch_peel(const GemmArgs& g, int peel, dim3 grid, hipStream_t stream) {
 // A kRing-deep ring needs at least kRing - 1 K stages: K >= 256 gives two.
 template <int EPI, int OUT>
 void launch_ring(const GemmArgs& g, dim3 grid, hipStream_t stream) {
-    static_assert(kRing - 1 <= kGemmKMultiple / kBK, "ring deeper than the shortest K");
+    static_assert(kRing - 1 <= kGemmKMin / kBK && kGemmKMultiple % kBK == 0, "ring deeper than the shortest K");
     const int kt_count = (int)(g.K / kBK);
     // With no stage to peel (K/128 - 2 a multiple of 3) the compiler copies
     // every accumulator on entering and leaving the unrolled loop (measured:

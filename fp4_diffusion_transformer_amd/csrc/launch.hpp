@@ -18,6 +18,10 @@ hipError_t launch_block_transform(const void* x, bool x_bf16, int64_t rows, int6
                                   const uint16_t* t, int64_t n_t, void* y, bool y_bf16,
                                   uint8_t* codes, uint8_t* scales, bool tiled, hipStream_t stream);
 
+hipError_t launch_relayout(const uint8_t* in_codes, const uint8_t* in_scales, bool in_tiled, int64_t rows,
+                           int64_t cols, uint8_t* out_codes, uint8_t* out_scales, bool out_tiled,
+                           hipStream_t stream);
+
 hipError_t launch_fold_inverse(const float* w, int64_t K, int64_t N, const uint16_t* t, int64_t n_t,
                                float* w_out, hipStream_t stream);
 
@@ -56,16 +60,14 @@ hipError_t launch_etd2(const void* x, const void* x0, const void* x0_prev, int64
 hipError_t launch_richardson(const void* fine, const void* coarse, int64_t n, int storage, float scale, void* out,
                              hipStream_t stream);
 
-// Shader-clock probe (measurement): per wave w of `workgroups` x 4 waves,
-// out[3w] shader-clock ticks and out[3w + 1] ticks of the 100 MHz counter
-// over `iters` rounds of 16 FP4 MFMAs, out[3w + 2] a checksum.
-hipError_t launch_clock_probe(uint64_t* out, int workgroups, int iters, hipStream_t stream);
-
 // Interleave group of the SwiGLU epilogue: channel blocks of 32 alternate
 // gate / up, matching one 32x32 MFMA output block per half.
 constexpr int kSwigluGroup = 32;
-// GEMM tiling constraints checked by the ABI layer.
+// GEMM tiling constraints checked by the ABI layer: N a multiple of the
+// 256-channel tile; K a multiple of the 128-deep LDS stage, and at least the
+// two stages the ring's prologue loads.
 constexpr int64_t kGemmNMultiple = 256;
-constexpr int64_t kGemmKMultiple = 256;
+constexpr int64_t kGemmKMultiple = 128;
+constexpr int64_t kGemmKMin = 256;
 
 }  // namespace fp4dit

@@ -50,6 +50,7 @@ def lib():
             "fp4dit_quantize_mxfp4": [P, I32, I64, I64, P, P, I32, P],
             "fp4dit_block_transform": [P, I32, I64, I64, P, I64, P, I32, P, P, I32, P],
             "fp4dit_fold_inverse_transform": [P, I64, I64, P, I64, P, P],
+            "fp4dit_mx_relayout": [P, P, I32, I64, I64, P, P, I32, P],
             "fp4dit_pack_weight": [P, I32, I64, I64, I32, P, P, I32, P],
             "fp4dit_gemm_fp4_epilogue_none": [I64, I64, I64, P, P, P, P, P, I32, P],
             "fp4dit_gemm_fp4_epilogue_rmsnorm_head": [I64, I64, I64, P, P, P, P, I32, I64, P, F, P, I32, P],
@@ -69,8 +70,6 @@ def lib():
         D, PD = ctypes.c_double, ctypes.POINTER(ctypes.c_double)
         L.fp4dit_etd_coefficients.argtypes = [D, D, D, D, I32, I32, PD, PD, PD]
         L.fp4dit_etd_coefficients.restype = ctypes.c_int
-        L.fp4dit_clock_probe.argtypes = [P, I32, I32, P]
-        L.fp4dit_clock_probe.restype = ctypes.c_int
         L.fp4dit_swiglu_interleave_group.argtypes = []
         L.fp4dit_swiglu_interleave_group.restype = ctypes.c_int32
         L.fp4dit_status_string.argtypes = [ctypes.c_int]
@@ -217,6 +216,18 @@ def block_transform(x, t, y_dtype=None, quantize=True, layout="tiled", y=None, o
           _ptr(mx.codes) if mx else None, _ptr(mx.scales) if mx else None,
           _LAYOUTS[mx.layout] if mx else TILED, _stream())
     return y, mx
+
+
+def mx_relayout(mx: MxTensor, layout="tiled", out: Optional[MxTensor] = None):
+    """The same MXFP4 values in another byte layout ("tiled": the GEMM's
+    operand layout; "rowmajor": plain codes [rows, cols/2], scales
+    [rows, cols/32])."""
+    _mx_check(mx, mx.rows, mx.cols, "mx")
+    res = _mx_check(out, mx.rows, mx.cols, "out") if out is not None else \
+        mx_empty(mx.rows, mx.cols, layout, mx.codes.device)
+    _call("fp4dit_mx_relayout", _ptr(mx.codes), _ptr(mx.scales), _LAYOUTS[mx.layout], mx.rows, mx.cols,
+          _ptr(res.codes), _ptr(res.scales), _LAYOUTS[res.layout], _stream())
+    return res
 
 
 def fold_inverse_transform(w, t):
@@ -443,28 +454,3 @@ def etd_coefficients(alpha_s, sigma_s, alpha_t, sigma_t, order=1, first_step=Fal
     _call("fp4dit_etd_coefficients", float(alpha_s), float(sigma_s), float(alpha_t), float(sigma_t), int(order),
           int(bool(first_step)), ctypes.byref(d), ctypes.byref(c0), ctypes.byref(c1))
     return d.value, c0.value, c1.value
-
-
-def clock_probe(out, workgroups=1, iters=64):
-    """Enqueue the shader-clock probe (a measurement helper, not a step of the
-    method) on the current stream: `workgroups` x 4 waves of FP4 MFMAs, each
-    wave writing its s_memtime and 100 MHz s_memrealtime ticks (and a
-    checksum) to 3 elements of the int64 device tensor `out`."""
-    if (out.dtype != torch.int64 or not out.is_cuda or not out.is_contiguous()
-            or out.numel() < 12 * int(workgroups)):
-        raise ValueError("clock_probe needs a contiguous int64 CUDA tensor of 12 elements per workgroup")
-    _call("fp4dit_clock_probe", out.data_ptr(), int(workgroups), int(iters), _stream())
-
-
-def clock_ghz(out, workgroups=1):
-    """Per-wave shader clocks (GHz) of a finished clock_probe."""
-    v = out.flatten()[:12 * int(workgroups)].cpu().reshape(-1, 3).tolist()
-    return [0.1 * t / r for t, r, _ in v if r > 0]
-
-
-def shader_clock_ghz(workgroups=1, iters=64):
-    """Median shader clock (GHz) over one probe on the current stream."""
-    out = torch.zeros(12 * int(workgroups), dtype=torch.int64, device="cuda")
-    clock_probe(out, workgroups, iters)
-    c = sorted(clock_ghz(out, workgroups))
-    return c[len(c) // 2] if c else float("nan")

@@ -142,6 +142,28 @@ fp4dit_status fp4dit_block_transform(const void* x, fp4dit_dtype x_dtype,
                                      hipStream_t stream);
 
 /*
+ * Re-layout of an MXFP4 tensor (KroQuant, "Deep analysis": the W4A4 format
+ * is MXFP4; fal, "Running the transformer in FP4": the e2m1 element) between
+ * FP4DIT_MX_ROWMAJOR and FP4DIT_MX_TILED, in either direction (the same
+ * layout on both sides is a copy).  Codes and scale bytes move; no value
+ * changes, so the result is unique (bit-exact).  A caller holding the plain
+ * row-major codes [rows][cols/2] and scales [rows][cols/32] gets the GEMM's
+ * operand layout this way.
+ *
+ * in_codes, in_scales    [rows][cols] in in_layout (buffer sizes as the
+ *                        layout states); out_codes, out_scales likewise in
+ *                        out_layout.  The padding rows of a TILED output
+ *                        (codes to round_up(rows, 2), scales to
+ *                        round_up(rows, 32)) are written as zero.
+ * cols % 128 == 0 if either side is TILED, else cols % 32 == 0; both codes
+ * pointers 16-byte aligned; no output buffer may overlap an input buffer or
+ * the other output (FP4DIT_E_UNSUPPORTED).
+ */
+fp4dit_status fp4dit_mx_relayout(const uint8_t* in_codes, const uint8_t* in_scales, fp4dit_layout in_layout,
+                                 int64_t rows, int64_t cols, uint8_t* out_codes, uint8_t* out_scales,
+                                 fp4dit_layout out_layout, hipStream_t stream);
+
+/*
  * Offline weight side of the block transform: W'_b = T_b^-1 . W_b.
  * KroQuant, "Background and overview" (the inverse transform goes to the
  * weights).
@@ -191,7 +213,8 @@ int32_t fp4dit_swiglu_interleave_group(void);
  * accumulation.  A = (a_codes, a_scales) is [M][K] and B = (b_codes,
  * b_scales) is [N][K], both in the FP4DIT_MX_TILED layout (buffers padded
  * as stated there); every codes pointer 16-byte aligned, every scales
- * pointer 4-byte aligned.  Requires K % 256 == 0 and K > 0,
+ * pointer 4-byte aligned.  Requires K % 128 == 0 and K >= 256 (the
+ * 128-deep K stage, and the two stages the LDS ring's prologue loads),
  * N % 256 == 0 and N > 0, and M*K/2 and N*K/2 below 2^31 bytes; M >= 0 is
  * otherwise arbitrary (a ragged last token tile is masked).
  */
@@ -355,22 +378,6 @@ fp4dit_status fp4dit_richardson_combine(const void* fine, const void* coarse, in
 fp4dit_status fp4dit_etd_coefficients(double alpha_s, double sigma_s, double alpha_t, double sigma_t,
                                       int32_t order, int32_t first_step, double* decay, double* c0,
                                       double* c1);
-
-/*
- * Measurement helper, no step of the method: the shader clock under a
- * scaled FP4 MFMA load.  `workgroups` workgroups of 4 waves (one per CU
- * loads the whole chip, as the persistent GEMM does) each run `iters`
- * rounds of 16 independent 32x32x64 FP4 MFMAs on pseudo-random operands.
- * Wave w writes, to the caller-owned device buffer `out` (3 uint64 per
- * wave, 8-byte aligned): out[3w] the ticks of the shader-clock counter
- * (s_memtime) and out[3w + 1] those of the constant 100 MHz counter
- * (s_memrealtime) over its MFMAs, out[3w + 2] a checksum.  Its clock in GHz
- * is 0.1 * out[3w] / out[3w + 1].  Enqueued on `stream`; the caller
- * synchronises.  Returns FP4DIT_E_NULL for a NULL `out`, FP4DIT_E_ALIGN for
- * a misaligned one, FP4DIT_E_SHAPE unless 1 <= workgroups <= 65536 and
- * 1 <= iters <= 2^20.
- */
-fp4dit_status fp4dit_clock_probe(uint64_t* out, int32_t workgroups, int32_t iters, hipStream_t stream);
 
 #ifdef __cplusplus
 }

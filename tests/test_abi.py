@@ -38,6 +38,7 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert len(names) == 18
+    assert "fp4dit_mx_relayout" in names and "fp4dit_clock_probe" not in names
     raw = ctypes.CDLL(ops.library_path())
     for n in names:
         assert hasattr(raw, n), n
@@ -66,7 +67,8 @@ def test_quantize_validation(L):
 def test_gemm_validation(L):
     g = L.fp4dit_gemm_fp4_epilogue_none
     assert g(256, 500, 512, P, P, P, P, P, BF16, None) == E_SHAPE         # N % 256
-    assert g(256, 512, 384, P, P, P, P, P, BF16, None) == E_SHAPE         # K % 256
+    assert g(256, 512, 320, P, P, P, P, P, BF16, None) == E_SHAPE         # K % 128
+    assert g(256, 512, 128, P, P, P, P, P, BF16, None) == E_SHAPE         # K >= 256
     assert g(256, 512, 0, P, P, P, P, P, BF16, None) == E_SHAPE
     assert g(-1, 512, 512, P, P, P, P, P, BF16, None) == E_SHAPE
     assert g(256, 512, 512, None, P, P, P, P, BF16, None) == E_NULL
@@ -172,8 +174,11 @@ def test_sizes_too_large_for_int64_products(L):
     assert L.fp4dit_fold_inverse_transform(P, 32 * big, big, P, 1, P + 64, None) == E_SHAPE
 
 
-def test_clock_probe_validation(L):
-    c = L.fp4dit_clock_probe
+def test_clock_probe_validation():
+    """The measurement helper lives in its own library, not in libfp4dit.so."""
+    from fp4_diffusion_transformer_amd import clockprobe
+    assert not hasattr(ctypes.CDLL(ops.library_path()), "fp4dit_clock_probe")
+    c = clockprobe.lib().fp4dit_clock_probe
     assert c(None, 1, 100, None) == E_NULL
     assert c(P + 4, 1, 100, None) == E_ALIGN
     assert c(P, 0, 100, None) == E_SHAPE
@@ -207,6 +212,24 @@ def test_etd_coefficients_host_logic(L):
     assert L.fp4dit_etd_coefficients(0.5, 0.0, 0.6, 0.4, 1, 0, ctypes.byref(d), ctypes.byref(c0),
                                      ctypes.byref(c1)) == E_SHAPE
     assert L.fp4dit_etd_coefficients(0.5, 0.5, 0.6, 0.4, 1, 0, None, ctypes.byref(c0), ctypes.byref(c1)) == E_NULL
+
+
+def test_relayout_validation(L):
+    r = L.fp4dit_mx_relayout
+    Q = P + (1 << 20)                                   # a second fake buffer, far from P
+    assert r(P, P + 4096, ROWMAJOR, 4, 96, Q, Q + 4096, TILED, None) == E_SHAPE     # tiled side: cols % 128
+    assert r(P, P + 4096, ROWMAJOR, 4, 80, Q, Q + 4096, ROWMAJOR, None) == E_SHAPE  # cols % 32
+    assert r(P, P + 4096, ROWMAJOR, -1, 128, Q, Q + 4096, TILED, None) == E_SHAPE
+    assert r(P, P + 4096, 3, 4, 128, Q, Q + 4096, TILED, None) == E_UNSUP
+    assert r(P, P + 4096, ROWMAJOR, 4, 128, Q, Q + 4096, 7, None) == E_UNSUP
+    assert r(None, P + 4096, ROWMAJOR, 4, 128, Q, Q + 4096, TILED, None) == E_NULL
+    assert r(P, P + 4096, ROWMAJOR, 4, 128, Q, None, TILED, None) == E_NULL
+    assert r(P_ODD, P + 4096, ROWMAJOR, 4, 128, Q, Q + 4096, TILED, None) == E_ALIGN
+    assert r(P, P + 4096, ROWMAJOR, 4, 128, Q + 8, Q + 4096, TILED, None) == E_ALIGN
+    assert r(P, P + 4096, ROWMAJOR, 4, 128, P, Q + 4096, TILED, None) == E_UNSUP    # output is the input
+    assert r(P, P + 4096, ROWMAJOR, 4, 128, P + 128, Q, TILED, None) == E_UNSUP     # overlaps the input
+    assert r(P, P + 4096, ROWMAJOR, 4, 128, Q, Q + 16, TILED, None) == E_UNSUP      # outputs overlap
+    assert r(None, None, ROWMAJOR, 0, 128, None, None, TILED, None) == OK          # empty
 
 
 def test_transform_pack_fold_validation(L):

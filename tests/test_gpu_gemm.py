@@ -307,3 +307,51 @@ def test_swiglu_transform_persistent_many_tiles_ragged():
     y, mx = ops.gemm_fp4_epilogue_swiglu_transform(*_dev_ops(*operands), dev(t, torch.bfloat16),
                                                    y_dtype=torch.float32)
     _check_fused(mx, y, c_g, c_u, t, rows=rows, what="persistent swiglu transform")
+
+
+# K a multiple of the 128-deep stage but not of 256: an odd number of K
+# stages (the ring's peel then covers 1, 3 or 2 stages)
+
+@pytest.mark.parametrize("k", [384, 640, 1152])
+@pytest.mark.parametrize("epilogue", ["none", "rmsnorm256", "swiglu_requant"])
+def test_k_odd_stage_count(epilogue, k):
+    rng = np.random.default_rng(71 + k)
+    m, n = 300, 768
+    announce("gemm odd K stages", epilogue, m, n, k)
+    if epilogue == "swiglu_requant":
+        operands, h_ref = _swiglu_operands(rng, m, n // 2, k)
+        h, mx = ops.gemm_fp4_epilogue_swiglu(*_dev_ops(*operands), out_dtype=torch.float32, requant=True)
+        parity.assert_close(host(h), h_ref, parity.TOL_F32, what="odd K swiglu")
+        codes = layout.untile_codes(host(mx.codes), mx.rows, mx.cols)
+        scales = layout.untile_scales(host(mx.scales), mx.rows, mx.cols)
+        exc, _ = parity.assert_codes_banded(codes, scales, h_ref, "odd K swiglu requant")
+        assert exc <= 0.001 * h_ref.size
+        return
+    ac, as_, bc, bs = _operands(rng, m, n, k)
+    c = ogemm.gemm(ac, as_, bc, bs)
+    if epilogue == "none":
+        out = ops.gemm_fp4_epilogue_none(*_dev_ops(ac, as_, bc, bs), out_dtype=torch.float32)
+        parity.assert_close(host(out), c, parity.TOL_F32, what="odd K none")
+    else:
+        norm_w = rng.uniform(0.5, 1.5, 512).astype(np.float32)
+        ref = ogemm.rmsnorm_head(c, 256, 512, norm_w.astype(np.float64), 1e-6)
+        out = ops.gemm_fp4_epilogue_rmsnorm_head(*_dev_ops(ac, as_, bc, bs), 256, 512, dev(norm_w, torch.float32),
+                                                 1e-6, out_dtype=torch.float32)
+        parity.assert_close(host(out), ref, parity.TOL_F32, group=256, what="odd K rmsnorm")
+
+
+def test_k_odd_stage_count_persistent_quarters():
+    """K = 384 on a persistent grid whose partial last round runs as quarter
+    tiles (384 tiles = 4 x 96 on 256 CUs), ragged last token tile."""
+    rng = np.random.default_rng(79)
+    m, n, k = 1000, 256 * 96, 384
+    rows = np.unique(np.concatenate([[0, 63, 64, 255, 768, 831, 832, 999], rng.choice(m, 40, replace=False)]))
+    announce("gemm odd K persistent quarters", m, n, k)
+    ac, as_, bc, bs = _operands(rng, m, n, k)
+    c = ogemm.gemm(ac[rows], as_[rows], bc, bs)
+    n_norm = n - 1024
+    norm_w = rng.uniform(0.5, 1.5, n_norm).astype(np.float32)
+    ref = ogemm.rmsnorm_head(c, 128, n_norm, norm_w.astype(np.float64), 1e-6)
+    out = ops.gemm_fp4_epilogue_rmsnorm_head(*_dev_ops(ac, as_, bc, bs), 128, n_norm, dev(norm_w, torch.float32),
+                                             1e-6, out_dtype=torch.bfloat16)
+    parity.assert_close(host(out)[rows], ref, parity.TOL_BF16, group=128, what="odd K quarters")

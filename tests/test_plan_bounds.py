@@ -23,7 +23,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SHAPES = [(256, 512, 512), (4096, 9216, 3072), (4096, 12288, 4096), (4096, 24576, 3072),
           (16384, 9216, 3072), (16384, 24576, 3072), (16384, 3072, 12288),
           (1, 256, 256), (255, 256, 512), (257, 512, 256), (600, 768, 1024), (1000, 20480, 256),
-          (1000, 20480, 512), (1000, 24576, 768), (1000, 256 * 80, 384), (64, 256, 384)]
+          (1000, 20480, 512), (1000, 24576, 768), (1000, 256 * 80, 384), (64, 256, 384),
+          (300, 768, 384), (300, 768, 640), (300, 768, 1152), (1000, 256 * 96, 384)]
 
 
 @pytest.fixture(scope="module")
