@@ -222,9 +222,11 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(kernel_key):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
+def traffic_from_profile(workload, kernel_key):
+    """Bytes per launch that leave the L2 (an upper bound on HBM bytes: no
+    counter separates Infinity Cache hits) from the committed rocprofv3
+    counter summary of this workload, if it was taken on the current kernel
+    sources; else None."""
     path = os.path.join(PROFILES, "hbm_traffic.json")
     if not os.path.exists(path):
         return None
@@ -232,7 +234,7 @@ def traffic_from_profile(kernel_key):
         rec = json.load(f)
     if rec.get("source_hash") != source_hash():
         return None
-    k = rec.get("kernels", {}).get(kernel_key)
+    k = rec.get("workloads", {}).get(workload, {}).get("kernels", {}).get(kernel_key)
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
@@ -667,7 +669,7 @@ def main():
             "peak": PEAK_MXFP4_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_MXFP4_TFLOPS, 4),
-            "traffic": traffic_from_profile(kernel_key),
+            "traffic": traffic_from_profile(args.workload, kernel_key),
             "avg_launch_ms": round(g_avg, 5),
             "algorithmic_bytes": Ld.gemm_bytes(),
         },

@@ -54,7 +54,8 @@ def _find(d, pattern):
 
 def kernel_key(name):
     """Short key of a kernel name (template arguments kept)."""
-    n = name.replace("fp4dit::(anonymous namespace)::", "").replace("fp4dit::", "")
+    n = name.replace("fp4dit::(anonymous namespace)::", "").replace("fp4dit::", "").replace(
+        "(anonymous namespace)::", "")
     for a, b in (("gemm_fp4_kernel<0,", "gemm_none<"), ("gemm_fp4_kernel<1,", "gemm_rmsnorm_head<"),
                  ("gemm_fp4_kernel<2,", "gemm_swiglu<"), ("gemm_fp4_kernel<3,", "gemm_swiglu_transform<")):
         n = n.replace(a, b)
@@ -111,10 +112,23 @@ def main(argv):
         traffic[key] = {"read_bytes": fr, "write_bytes": wr}
     with open(out_txt, "w") as f:
         f.write("\n".join(lines) + "\n")
-    rec = {"source_hash": source_hash(), "copy_mib": copy_mib, "fetch_factor": f_fac, "write_factor": w_fac,
-           "kernels": {k: {"hbm_bytes_per_launch": v["read_bytes"] + v["write_bytes"], **v}
-                       for k, v in traffic.items()}}
-    with open(os.path.join(ROOT, "profiles", "hbm_traffic.json"), "w") as f:
+    # one record per workload (the summary's name kernels_<workload>.txt): the
+    # same kernel instantiation runs at other sizes in other workloads
+    base = os.path.basename(out_txt)
+    workload = base[len("kernels_"):-len(".txt")] if base.startswith("kernels_") and base.endswith(".txt") else base
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    rec = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            rec = json.load(f)
+    if rec.get("source_hash") != source_hash() or "workloads" not in rec:
+        rec = {"source_hash": source_hash(), "workloads": {}}
+    rec["note"] = ("bytes that leave the L2 per launch (reads that miss it, writes sent on): requests to the "
+                   "memory side, served by the Infinity Cache or HBM; an upper bound on HBM bytes")
+    rec["workloads"][workload] = {
+        "copy_mib": copy_mib, "fetch_factor": f_fac, "write_factor": w_fac,
+        "kernels": {k: {"hbm_bytes_per_launch": v["read_bytes"] + v["write_bytes"], **v} for k, v in traffic.items()}}
+    with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     print("\n".join(lines))
 

@@ -40,7 +40,7 @@ def test_calibration_uses_the_largest_fill_and_sum(tmp_path, monkeypatch):
         ("void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<long> >", "WRITE_SIZE", 0.09),
         ("void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float> >", "WRITE_SIZE", kib),
         (gemm, "WRITE_SIZE", 100.0)])
-    out = str(tmp_path / "summary.txt")
+    out = str(tmp_path / "kernels_some_workload.txt")
     written = {}
     real_open = open
 
@@ -60,7 +60,7 @@ def test_calibration_uses_the_largest_fill_and_sum(tmp_path, monkeypatch):
 
     monkeypatch.setattr("builtins.open", fake_open)
     profsum.main(["profsum", trace, fetch, write, out, str(mib)])
-    rec = json.loads(written["json"])
+    rec = json.loads(written["json"])["workloads"]["some_workload"]
     assert abs(rec["fetch_factor"] - 2.0) < 1e-12 and abs(rec["write_factor"] - 1.0) < 1e-12
     k = rec["kernels"]["gemm_swiglu<0,3,1>"]
     assert k["read_bytes"] == 1000.0 * 1024 * 2 and k["write_bytes"] == 100.0 * 1024
