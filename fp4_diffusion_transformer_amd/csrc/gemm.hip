@@ -287,12 +287,17 @@ __device__ __forceinline__ void tile_of(int bid, int nwg, int tiles_n, int tiles
 // that every global store writes whole row segments.  vals(q, v) gives the
 // lane's 4 fp32 values of 8-column chunk q (half h) for token tok0 + r32.
 // Token rows sit kRowPad = 16Q + 16 bytes apart: the 16-byte pad rotates
-// consecutive rows by four banks, so the 16-byte row reads are free of bank
-// conflicts; the 8-byte writes put rows r and r + 16 on the same banks
+// consecutive rows by four banks.  A lane holds half of each 16-byte chunk
+// (4 of its 8 columns; its partner lane l ^ 32 the other half), and the 16
+// lanes of a quarter-wave hold 16 different rows of one half, so 8-byte
+// writes of the halves put rows r and r + 8 on the same banks
 // (SQ_LDS_BANK_CONFLICT: about 12% of the RMSNorm GEMMs' LDS-active cycles).
-// An 8-byte pad with the rows read back in 8-byte halves took a third of
-// those conflicts away and no time.  All accesses of a lane share one base
-// address (immediate offsets).  Only this wave touches `region`
+// Instead, for each pair of chunks (2p, 2p + 1) one v_permlane32_swap per
+// dword hands lane h = 0 the whole chunk 2p and lane h = 1 the whole chunk
+// 2p + 1: one 16-byte write per lane and pair, every group of 8 lanes on
+// distinct banks, and half as many LDS writes.  The row reads are 16 bytes
+// per lane, conflict-free with the same pad.  All accesses of a lane share
+// one base address (immediate offsets).  Only this wave touches `region`
 // (32 * kRowPad bytes).
 template <int Q>
 constexpr int row_pad_bytes() { return Q * 16 + 16; }
@@ -300,16 +305,24 @@ constexpr int row_pad_bytes() { return Q * 16 + 16; }
 template <int Q, typename F>
 __device__ __forceinline__ void store_bf16_half(uint8_t* region, F vals, uint16_t* out, int64_t ld,
                                                 int64_t tok0, int64_t col0, int64_t M, int r32, int h, int lane) {
+    static_assert(Q % 2 == 0, "chunks go in pairs");
     constexpr int kRowPad = row_pad_bytes<Q>();
-    uint8_t* wbase = region + r32 * kRowPad + h * 8;
+    uint8_t* wbase = region + r32 * kRowPad + h * 16;
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        float v[4];
-        vals(q, v);
-        v2u o;
-        o[0] = pack_bf16x2(v[0], v[1]);
-        o[1] = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<v2u*>(wbase + q * 16) = o;
+    for (int p = 0; p < Q / 2; ++p) {
+        float va[4], vb[4];
+        vals(2 * p, va);
+        vals(2 * p + 1, vb);
+        // this lane's 4 columns (half h) of chunks 2p (a) and 2p + 1 (b)
+        const uint32_t a0 = pack_bf16x2(va[0], va[1]), a1 = pack_bf16x2(va[2], va[3]);
+        const uint32_t b0 = pack_bf16x2(vb[0], vb[1]), b1 = pack_bf16x2(vb[2], vb[3]);
+        // swap(a, b): lanes 0..31 keep a and receive the partner's a, lanes
+        // 32..63 receive the partner's b and keep b -- i.e. {x[0], y[0]} is
+        // the whole chunk 2p + h as (low 4 columns, high 4 columns)
+        const auto x = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+        const auto y = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+        const v4u o = {x[0], y[0], x[1], y[1]};
+        *reinterpret_cast<v4u*>(wbase + p * 32) = o;
     }
     wave_lds_fence();
     // Read back all of the wave's rows before the first store: one wait for
