@@ -355,3 +355,32 @@ def test_k_odd_stage_count_persistent_quarters():
     out = ops.gemm_fp4_epilogue_rmsnorm_head(*_dev_ops(ac, as_, bc, bs), 128, n_norm, dev(norm_w, torch.float32),
                                              1e-6, out_dtype=torch.bfloat16)
     parity.assert_close(host(out)[rows], ref, parity.TOL_BF16, group=128, what="odd K quarters")
+
+
+def test_largest_operand_size():
+    """The largest M the 32-bit operand offsets allow at K = 256 (the token
+    codes just under 2^31 bytes), plain epilogue, bf16 out (an 8.6 GB
+    output).  A is a 4096-row block repeated (its tiled bytes repeat every
+    2048 row pairs and 128 scale blocks), so the oracle's rows are rows of
+    the block; sampled rows at both ends and around 2^24."""
+    k, n, blk = 256, 256, 4096
+    m = ((2 ** 31 - 1) // (k // 2)) & ~1                  # even: codes of m rows < 2^31 bytes
+    m -= m % blk                                           # whole repeats of the block
+    assert (m + 1) * (k // 2) <= 2 ** 31 - 1
+    rng = np.random.default_rng(83)
+    ac, as_, bc, bs = _operands(rng, blk, n, k)
+    tc = torch.from_numpy(layout.tile_codes(mxfp4.pack_codes(ac)))
+    ts = torch.from_numpy(layout.tile_scales(as_))
+    reps = m // blk
+    announce("gemm largest operand", m, n, k)
+    a = ops.MxTensor(tc.to("cuda").repeat(reps, 1), ts.to("cuda").repeat(reps, 1), m, k, "tiled")
+    b = _mx(bc, bs)
+    out = ops.gemm_fp4_epilogue_none(a, b, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, blk - 1, blk, m // 2, 2 ** 24 - 1, 2 ** 24, m - blk, m - 2, m - 1],
+                                     rng.choice(m, 16, replace=False)]))
+    rows = rows[rows < m]
+    got = out[torch.from_numpy(rows).to("cuda")].float().cpu().numpy().astype(np.float64)
+    del out, a
+    ref = ogemm.gemm(ac[rows % blk], as_[rows % blk], bc, bs)
+    parity.assert_close(got, ref, parity.TOL_BF16, what="largest operand")
