@@ -123,3 +123,29 @@ def test_pack_weight_swiglu_interleave():
     phys = ogemm.interleave_weight(wg, wu, g)
     rc, rs = mxfp4.quantize(phys.astype(np.float64).T)
     parity.assert_codes_exact(gc, gs, rc, rs, "pack interleaved")
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 64), (1, 96), (5, 160), (7, 512)])
+@pytest.mark.parametrize("offset", [0, 1, 2, 3])
+def test_scale_stores_at_any_alignment(rows, cols, offset):
+    """Scale bytes go out four at a time when the scale buffer is 4-byte
+    aligned, one at a time otherwise (the ABI does not require alignment)
+    and for a last group of fewer than four blocks: every case must write
+    exactly the oracle's bytes and nothing outside the buffer."""
+    rng = np.random.default_rng(rows * 13 + cols + offset)
+    x = (rng.standard_normal((rows, cols)) * 2.0 ** rng.integers(-8, 8, (rows, 1))).astype(np.float32)
+    rc, rs = mxfp4.quantize(x.astype(np.float64))
+    n = rows * (cols // 32)
+    announce("quantize scale stores", rows, cols, offset)
+    xd = dev(x, torch.float32)
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda")
+    buf = torch.full((n + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+    st = ops.lib().fp4dit_quantize_mxfp4(xd.data_ptr(), ops.F32, rows, cols, codes.data_ptr(),
+                                         buf.data_ptr() + 16 + offset, ops.ROWMAJOR,
+                                         torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    b = host(buf)
+    parity.assert_codes_exact(host(codes), b[16 + offset:16 + offset + n].reshape(rows, cols // 32), rc, rs,
+                              "scales at offset %d" % offset)
+    assert (b[:16 + offset] == 0xA5).all() and (b[16 + offset + n:] == 0xA5).all(), "bytes outside the scales"
