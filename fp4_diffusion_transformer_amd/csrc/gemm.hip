@@ -166,8 +166,9 @@ using plan::make_plan;
 using plan::make_qplan;
 
 // Buffer descriptors of the four operand arrays (scalar registers, set up
-// once): every load of a stage then adds the same scalar offset kt * 128 to
-// its fixed per-lane offset.  The record counts are the arrays' sizes.
+// once): every load of a stage then adds the stage's scalar offset
+// (stage * 128) to its fixed per-lane offset.  The record counts are the
+// arrays' sizes.
 struct Operands {
     __amdgpu_buffer_rsrc_t wc, xc, ws, xs;
 };
@@ -186,12 +187,12 @@ __device__ __forceinline__ Operands make_operands(const GemmArgs& g) {
     return o;
 }
 
-// Enqueue the 10 direct-to-LDS loads of K stage kt (this wave's share).
-// codes / scales: LDS byte addresses of this wave's part of the stage's code
-// and scale areas (stage + wave * 4096, stage + wave * 256).
+// Enqueue the 10 direct-to-LDS loads of the K stage at scalar offset soff
+// (stage * 128; this wave's share).  codes / scales: LDS byte addresses of
+// this wave's part of the stage's code and scale areas (stage + wave * 4096,
+// stage + wave * 256).
 __device__ __forceinline__ void issue_stage(uint32_t codes, uint32_t scales, const Operands& o, const LoadPlan& p,
-                                            int kt) {
-    const uint32_t soff = (uint32_t)kt * 128u;
+                                            uint32_t soff) {
     auto lds = [](uint32_t a) { return (lds_void*)(uintptr_t)a; };
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -229,11 +230,11 @@ __device__ __forceinline__ void issue_load(int l, uint32_t codes, uint32_t scale
 }
 
 // Whole-stage prefetch outside the K loop (prologue of a tile).
-__device__ __forceinline__ void issue_stage_at(uint8_t* stage, const Operands& o, const LoadPlan& p, int kt,
+__device__ __forceinline__ void issue_stage_at(uint8_t* stage, const Operands& o, const LoadPlan& p, uint32_t soff,
                                                int wave) {
     const uint32_t codes = opaque_sgpr(lds_addr(stage) + wave * 4096);
     const uint32_t scales = opaque_sgpr(lds_addr(stage) + wave * 256);
-    issue_stage(codes, scales, o, p, kt);
+    issue_stage(codes, scales, o, p, soff);
 }
 
 struct Frags {
@@ -401,7 +402,8 @@ __device__ __forceinline__ void read_scale(uint32_t* wsc, uint32_t* xsc, const u
 template <bool ISSUE, bool NEXT, int VM>
 __device__ __forceinline__ void k_stage(v16f (&acc)[4][4], Frags& f0, Frags& f1, uint32_t* wsc, uint32_t* xsc,
                                         uint8_t* cur_, uint8_t* nxt_, uint8_t* fill, const Operands& ops,
-                                        const LoadPlan& plan, int kt, int wave, int wn, int wm, int r32, int h) {
+                                        const LoadPlan& plan, const plan::KOrder& ko, int kt, int wave, int wn, int wm,
+                                        int r32, int h) {
     // The stage's LDS bases, made opaque in one statement ahead of all its
     // memory operations: the compiler then forms each address at its use
     // (one add) instead of keeping one live register per ring slot and load.
@@ -409,7 +411,7 @@ __device__ __forceinline__ void k_stage(v16f (&acc)[4][4], Frags& f0, Frags& f1,
     asm volatile("" : "+s"(fill_codes), "+s"(fill_scales), "+s"(zero));
     const uint8_t* cur = cur_ + zero;
     const uint8_t* nxt = nxt_ + zero;
-    const uint32_t soff = (uint32_t)(kt + kRing - 1) * 128u;
+    const uint32_t soff = plan::stage_soff(ko, kt + kRing - 1);
     static_for<0, 16>([&](auto n) {
         constexpr int kN = decltype(n)::value;
         mfma_one<0>(acc[kN / 4][kN % 4], f0.w[kN / 4], f0.x[kN % 4], wsc[kN / 4], xsc[kN % 4]);
@@ -928,10 +930,14 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
     int v = blockIdx.x;
     bool relaxed = false;
     int tm, tn;
+    int nth = 0;                                       // tiles this workgroup has started
+    plan::KOrder ko = plan::k_order(nth, kt_count);
     tile_of(v, n_tiles, tiles_n, tiles_m, tm, tn);
     {
         const LoadPlan plan = make_plan(M, K, tn * kBN, tm * kBM, wave, fresh_lane_id());
-        static_for<0, D>([&](auto j) { issue_stage_at(slots[(j() + OFF) % NS], ops, plan, j(), wave); });
+        static_for<0, D>([&](auto j) {
+            issue_stage_at(slots[(j() + OFF) % NS], ops, plan, plan::stage_soff(ko, j()), wave);
+        });
     }
 
     for (;;) {
@@ -967,14 +973,14 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
         // stages 0 .. PEEL-1 (each issues the loads of stage j + D)
         static_for<0, PEEL>([&](auto j) {
             k_stage<true, true, kVmSteady>(acc, f0, f1, wsc, xsc, slots[(j() + OFF) % NS],
-                                           slots[(j() + OFF + 1) % NS], slots[(j() + OFF + D) % NS], ops, plan, j(),
+                                           slots[(j() + OFF + 1) % NS], slots[(j() + OFF + D) % NS], ops, plan, ko, j(),
                                            wave, wn, wm, r32, h);
         });
         // stages PEEL .. kt_count - NS, NS at a time, on slots 0 .. NS-1
         for (int kt = PEEL; kt < n_issue; kt += NS) {
             static_for<0, NS>([&](auto s) {
                 k_stage<true, true, kVmSteady>(acc, f0, f1, wsc, xsc, slots[s()], slots[(s() + 1) % NS],
-                                               slots[(s() + D) % NS], ops, plan, kt + s(), wave, wn, wm, r32, h);
+                                               slots[(s() + D) % NS], ops, plan, ko, kt + s(), wave, wn, wm, r32, h);
             });
         }
         // the last D stages: no more loads; stage n_issue + i waits for the
@@ -983,13 +989,14 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
             constexpr int kI = decltype(i)::value;
             constexpr int kVm = kI < D - 1 ? (D - 2 - kI) * kDmaPerStage : 0;
             k_stage<false, (kI < D - 1), kVm>(acc, f0, f1, wsc, xsc, slots[kI], slots[(kI + 1) % NS], slots[0], ops,
-                                              plan, n_issue + kI, wave, wn, wm, r32, h);
+                                              plan, ko, n_issue + kI, wave, wn, wm, r32, h);
         });
         ring_barrier<63>();                            // every wave is done reading the ring
 
         const int vn = v + (int)gridDim.x;
         const bool more = vn < n_full;                 // the next tile is a full one
         if (more) tile_of(vn, n_tiles, tiles_n, tiles_m, tm, tn);
+        ko = plan::k_order(++nth, kt_count);           // the next tile's K order
         // finish this tile; the next full tile's first stages load meanwhile
         // (their load offsets are formed there rather than kept live through
         // the epilogue)
@@ -998,13 +1005,16 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
             [&]() {
                 if (kEarly && more) {
                     const LoadPlan pl = make_plan(M, K, tn * kBN, tm * kBM, wave, fresh_lane_id());
-                    static_for<0, D>([&](auto j) { issue_stage_at(slots[(j() + OFF) % NS], ops, pl, j(), wave); });
+                    static_for<0, D>([&](auto j) {
+                        issue_stage_at(slots[(j() + OFF) % NS], ops, pl, plan::stage_soff(ko, j()), wave);
+                    });
                 }
             },
             [&](int mb) {
                 if (!kEarly && more && mb < D)
                     issue_stage_at(slots[(mb + OFF) % NS], ops,
-                                   make_plan(M, K, tn * kBN, tm * kBM, wave, fresh_lane_id()), mb, wave);
+                                   make_plan(M, K, tn * kBN, tm * kBM, wave, fresh_lane_id()),
+                                   plan::stage_soff(ko, mb), wave);
             });
         if (!more) {
             if constexpr (kEarly) v = vn;              // on to the quarter tiles

@@ -81,6 +81,22 @@ __host__ __device__ __forceinline__ QPlan make_qplan(int M, int K, int n0, int m
     return p;
 }
 
+// K order of a full tile.  A workgroup walks K upwards in its even-numbered
+// tiles and downwards in its odd-numbered ones; the workgroups of one XCD
+// run their n-th tiles together, so each round starts on the K stages the
+// round before finished on, which are still in that XCD's L2.  Position i
+// of the tile's K loop fetches stage base + i * step (in bytes of the
+// stage's 128-byte tile); both are uniform scalars.
+struct KOrder {
+    int32_t base, step;
+};
+__host__ __device__ __forceinline__ KOrder k_order(int tile_index, int kt_count) {
+    return (tile_index & 1) ? KOrder{(kt_count - 1) * 128, -128} : KOrder{0, 128};
+}
+__host__ __device__ __forceinline__ uint32_t stage_soff(const KOrder& o, int i) {
+    return (uint32_t)(o.base + i * o.step);
+}
+
 // The quarter loop keeps kQDepth stages in flight and gives every stage the
 // same body, so near the end of K (and in the prologue when K has fewer
 // stages than that) it still issues loads for stages past the last one.

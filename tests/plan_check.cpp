@@ -2,8 +2,8 @@
 // built from the kernel's own load-plan code (csrc/gemm_plan.hpp).
 //
 // For each GEMM shape M N K given on the command line, every 256 x 256 tile
-// and every 256 x 64 quarter of it, every wave and lane, and every K stage a
-// load is issued for, the byte range a load reads must lie inside the
+// (in both of its K orders) and every 256 x 64 quarter of it, every wave and
+// lane, and every K stage a load is issued for, the byte range a load reads must lie inside the
 // operand buffer (the tiled buffer size, which is also the record count of
 // the kernel's buffer descriptor).  The scalar stage offset of these buffer
 // loads is not range-checked by the hardware, so this is the only guard.
@@ -17,6 +17,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <vector>
 
 #include "gemm_plan.hpp"
 
@@ -35,8 +36,25 @@ static bool in_range(const char* what, int64_t off, int width, int64_t bytes, in
     return true;
 }
 
+// Each K order visits every stage exactly once, on 128-byte stage boundaries.
+static bool check_orders(int kt_count) {
+    for (int nth = 0; nth < 2; ++nth) {
+        const KOrder ko = k_order(nth, kt_count);
+        std::vector<int> seen(kt_count, 0);
+        for (int i = 0; i < kt_count; ++i) {
+            const int64_t so = (int64_t)(int32_t)stage_soff(ko, i);
+            if (so < 0 || so % kBK != 0 || so / kBK >= kt_count || seen[so / kBK]++) {
+                std::printf("K order %d: position %d gives offset %lld (%d stages)\n", nth, i, (long long)so, kt_count);
+                return false;
+            }
+        }
+    }
+    return true;
+}
+
 static bool check_shape(int M, int N, int K, bool unclamped) {
     const int kt_count = K / kBK;
+    if (!check_orders(kt_count)) return false;
     const int64_t wc = code_bytes(N, K), xc = code_bytes(M, K), ws = scale_bytes(N, K), xs = scale_bytes(M, K);
     const int tiles_n = N / 256, tiles_m = (M + 255) / 256;
     // the extreme stages suffice for the large shapes (offsets grow with the stage)
@@ -46,18 +64,23 @@ static bool check_shape(int M, int N, int K, bool unclamped) {
             const int n0 = tn * 256, m0 = tm * 256;
             for (int wave = 0; wave < 4; ++wave)
                 for (int lane = 0; lane < 64; ++lane) {
-                    // full tile: stages 0 .. kt_count - 1 (the prefetch of a tile's
-                    // first stages included)
+                    // full tile: K positions 0 .. kt_count - 1 (the prefetch of a
+                    // tile's first stages included), in both K orders (a
+                    // workgroup's even and odd tiles)
                     const LoadPlan p = make_plan(M, K, n0, m0, wave, lane);
-                    for (int kt = 0; kt < kt_count; ++kt) {
-                        if (!all_stages && kt != 0 && kt != kt_count - 1) continue;
-                        const int64_t so = (int64_t)kt * kBK;
-                        for (int j = 0; j < 4; ++j) {
-                            if (!in_range("weight codes", p.w_code[j] + so, 16, wc, n0, m0, wave, lane, kt)) return false;
-                            if (!in_range("token codes", p.x_code[j] + so, 16, xc, n0, m0, wave, lane, kt)) return false;
+                    for (int nth = 0; nth < 2; ++nth) {
+                        const KOrder ko = k_order(nth, kt_count);
+                        for (int i = 0; i < kt_count; ++i) {
+                            if (!all_stages && i != 0 && i != kt_count - 1) continue;
+                            const int64_t so = (int64_t)(int32_t)stage_soff(ko, i);
+                            const int kt = (int)(so / kBK);
+                            for (int j = 0; j < 4; ++j) {
+                                if (!in_range("weight codes", p.w_code[j] + so, 16, wc, n0, m0, wave, lane, kt)) return false;
+                                if (!in_range("token codes", p.x_code[j] + so, 16, xc, n0, m0, wave, lane, kt)) return false;
+                            }
+                            if (!in_range("weight scales", p.w_scale + so, 4, ws, n0, m0, wave, lane, kt)) return false;
+                            if (!in_range("token scales", p.x_scale + so, 4, xs, n0, m0, wave, lane, kt)) return false;
                         }
-                        if (!in_range("weight scales", p.w_scale + so, 4, ws, n0, m0, wave, lane, kt)) return false;
-                        if (!in_range("token scales", p.x_scale + so, 4, xs, n0, m0, wave, lane, kt)) return false;
                     }
                     // quarter tiles: load positions 0 .. kt_count + kQDepth - 1
                     // (the prologue's kQDepth stages, then stage kt + kQDepth

@@ -2,10 +2,11 @@
 
 The GEMM's loads add a scalar stage offset that the hardware's range check
 does not cover, so an out-of-range stage would read past the caller's
-buffer.  tests/plan_check.cpp walks every load of a launch -- full tiles,
-quarter tiles, every wave, lane and stage -- using the kernel's own plan
-code (csrc/gemm_plan.hpp, compiled for the host), against the tiled buffer
-sizes.  Runs on the CPU.
+buffer.  tests/plan_check.cpp walks every load of a launch -- full tiles in
+both of their K orders, quarter tiles, every wave, lane and stage -- using
+the kernel's own plan code (csrc/gemm_plan.hpp, compiled for the host),
+against the tiled buffer sizes, and checks that each K order visits every
+stage once.  Runs on the CPU.
 """
 
 import os
