@@ -338,6 +338,11 @@ __device__ __forceinline__ void store_bf16_half(uint8_t* region, F vals, uint16_
     v4u rows[kIts];
 #pragma unroll
     for (int it = 0; it < kIts; ++it) rows[it] = *reinterpret_cast<const v4u*>(rbase + it * kRowsPerInst * kRowPad);
+    // all rows held at once: without this the register allocator (the file
+    // is nearly full here) reuses one row's registers for the next, which
+    // puts a full LDS round trip before every store
+#pragma unroll
+    for (int it = 0; it < kIts; ++it) asm volatile("" : "+v"(rows[it]));
     const int64_t valid = M - tok0 < 0 ? 0 : (M - tok0 < 32 ? M - tok0 : 32);
     const __amdgpu_buffer_rsrc_t o =
         buffer_rsrc(reinterpret_cast<const uint8_t*>(out + tok0 * ld + col0), valid * ld * 2);
@@ -585,14 +590,19 @@ __device__ __forceinline__ void epilogue(v16f (&acc)[4][MB], const GemmArgs& g, 
             // result would be kept live in a VGPR across the main loop
             const float inv_d = g.head_dim == 256 ? 1.0f / 256.0f : 1.0f / 128.0f;
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) rstd[mb] = rsqrtf(ss[mb] * inv_d + g.eps);
+            for (int mb = 0; mb < MB; ++mb) rstd[mb] = norm ? rsqrtf(ss[mb] * inv_d + g.eps) : 1.f;
         }
+        // Columns past n_norm pass through as C * 1 * 1, which is C exactly
+        // (rstd and the gains are 1 there), so the bf16 path needs no
+        // per-value select (256 fewer VALU per tile); the fp32 path keeps it
+        // (without it the compiler spills in one of its instantiations).
         auto vals = [&](int q, int mb, float* v) {
             const int nb = q >> 2, a = q & 3;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                v[r] = (EPI == kEpiRmsNorm && norm) ? acc[nb][mb][4 * a + r] * rstd[mb] * wv[nb][a][r]
-                                                    : acc[nb][mb][4 * a + r];
+                v[r] = (EPI == kEpiRmsNorm && (OUT == kOutBf16 || norm))
+                           ? acc[nb][mb][4 * a + r] * rstd[mb] * wv[nb][a][r]
+                           : acc[nb][mb][4 * a + r];
         };
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
