@@ -404,7 +404,7 @@ __device__ __forceinline__ void read_scale(uint32_t* wsc, uint32_t* xsc, const u
 //   and the 8 scale then 8 fragment reads of stage kt+1 one per MFMA.
 // Measured against packing the loads into the first 10 slots, reads into the
 // first 8 of K-step 1, or loading after the barrier: about 2% faster.
-template <bool ISSUE, bool NEXT, int VM>
+template <bool ISSUE, bool NEXT, int VM, bool MB_MAJOR = false>
 __device__ __forceinline__ void k_stage(v16f (&acc)[4][4], Frags& f0, Frags& f1, uint32_t* wsc, uint32_t* xsc,
                                         uint8_t* cur_, uint8_t* nxt_, uint8_t* fill, const Operands& ops,
                                         const LoadPlan& plan, const plan::KOrder& ko, int kt, int wave, int wn, int wm,
@@ -428,7 +428,10 @@ __device__ __forceinline__ void k_stage(v16f (&acc)[4][4], Frags& f0, Frags& f1,
     if (NEXT) ring_barrier<VM>();
     static_for<0, 16>([&](auto n) {
         constexpr int kN = decltype(n)::value;
-        mfma_one<1>(acc[kN / 4][kN % 4], f1.w[kN / 4], f1.x[kN % 4], wsc[kN / 4], xsc[kN % 4]);
+        // the tile's last K-step may go token block by token block, so the
+        // epilogue's first token block can start while the rest finish
+        constexpr int kNb = MB_MAJOR ? kN % 4 : kN / 4, kMb = MB_MAJOR ? kN / 4 : kN % 4;
+        mfma_one<1>(acc[kNb][kMb], f1.w[kNb], f1.x[kMb], wsc[kNb], xsc[kMb]);
         constexpr int kLate = kN - 6;                          // late loads in slots 6, 7
         if constexpr (ISSUE && kLate >= 0 && kLate < kDmaPerStage - kDmaEarly)
             issue_load(kDmaEarly + kLate, fill_codes, fill_scales, ops, plan, soff);
@@ -998,9 +1001,21 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(GemmArgs g) {
         static_for<0, D>([&](auto i) {
             constexpr int kI = decltype(i)::value;
             constexpr int kVm = kI < D - 1 ? (D - 2 - kI) * kDmaPerStage : 0;
-            k_stage<false, (kI < D - 1), kVm>(acc, f0, f1, wsc, xsc, slots[kI], slots[(kI + 1) % NS], slots[0], ops,
-                                              plan, ko, n_issue + kI, wave, wn, wm, r32, h);
+            k_stage<false, (kI < D - 1), kVm, (kI == D - 1)>(acc, f0, f1, wsc, xsc, slots[kI], slots[(kI + 1) % NS],
+                                                             slots[0], ops, plan, ko, n_issue + kI, wave, wn, wm,
+                                                             r32, h);
         });
+        // All 16 accumulator blocks pass through one empty asm statement:
+        // every last MFMA issues before the epilogue reads any accumulator.
+        // Otherwise the scheduler puts reads of a just-written block between
+        // the last MFMAs, and each such read holds the wave's issue until
+        // that MFMA has finished, so the next MFMA waits too.  With the last
+        // K-step ordered by token block, block 0's results are ready first.
+        asm volatile(""
+                     : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]), "+a"(acc[1][0]),
+                       "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]), "+a"(acc[2][0]), "+a"(acc[2][1]),
+                       "+a"(acc[2][2]), "+a"(acc[2][3]), "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]),
+                       "+a"(acc[3][3]));
         ring_barrier<63>();                            // every wave is done reading the ring
 
         const int vn = v + (int)gridDim.x;
