@@ -37,6 +37,11 @@
 //   2h + s, so a lane's two scale bytes of a stage are adjacent; one LDS
 //   read fetches them and op_sel picks the byte.  Both operands use
 //   the same permutation, so the sum over K is unchanged.
+// * Persistent grid, one workgroup per CU, tiles in an XCD-aware order; a
+//   workgroup's K loop alternates direction from tile to tile (up, down,
+//   ...), so each round of tiles starts on the K stages the previous round
+//   left in the XCD's L2.  Below, "stage kt" is position kt of the tile's
+//   K order; plan::stage_soff gives the stage it fetches.
 // * bf16 outputs go through LDS (after the main loop) so that every global
 //   store writes whole row segments.
 #include <atomic>

@@ -33,7 +33,8 @@ __host__ __device__ __forceinline__ int64_t scale_bytes(int64_t rows, int64_t K)
 // the 256 token rows; one instruction moves 16 rows x 64 B (lane: row
 // lane/4, 16-byte chunk lane%4, written at its swizzled LDS position), the
 // scale instructions 64 rows x 4 B.  Token rows past M are clamped to row
-// M - 1 (loaded, never stored).  The K stage adds kt * 128 to every offset.
+// M - 1 (loaded, never stored).  A K stage adds its offset (stage * 128,
+// see stage_soff) to every offset.
 struct LoadPlan {
     uint32_t w_code[4], x_code[4];
     uint32_t w_scale, x_scale;
