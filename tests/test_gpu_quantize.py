@@ -128,10 +128,9 @@ def test_pack_weight_swiglu_interleave():
 @pytest.mark.parametrize("rows,cols", [(1, 64), (1, 96), (5, 160), (7, 512)])
 @pytest.mark.parametrize("offset", [0, 1, 2, 3])
 def test_scale_stores_at_any_alignment(rows, cols, offset):
-    """Scale bytes go out four at a time when the scale buffer is 4-byte
-    aligned, one at a time otherwise (the ABI does not require alignment)
-    and for a last group of fewer than four blocks: every case must write
-    exactly the oracle's bytes and nothing outside the buffer."""
+    """The row-major scales buffer needs no alignment (the ABI does not ask
+    for any): at every byte offset the kernel must write exactly the
+    oracle's bytes and nothing outside the buffer."""
     rng = np.random.default_rng(rows * 13 + cols + offset)
     x = (rng.standard_normal((rows, cols)) * 2.0 ** rng.integers(-8, 8, (rows, 1))).astype(np.float32)
     rc, rs = mxfp4.quantize(x.astype(np.float64))
@@ -149,3 +148,35 @@ def test_scale_stores_at_any_alignment(rows, cols, offset):
     parity.assert_codes_exact(host(codes), b[16 + offset:16 + offset + n].reshape(rows, cols // 32), rc, rs,
                               "scales at offset %d" % offset)
     assert (b[:16 + offset] == 0xA5).all() and (b[16 + offset + n:] == 0xA5).all(), "bytes outside the scales"
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("rows,cols", [(1, 128), (31, 128), (33, 640), (95, 384), (1001, 2048), (4101, 1024)])
+def test_tiled_stores_stay_inside(dtype, rows, cols):
+    """Tiled output with ragged rows: with guard bytes around both tiled
+    buffers, the real rows hold the oracle's bytes and nothing is written
+    outside the buffers (the padding rows inside them are the library's to
+    leave or fill)."""
+    rng = np.random.default_rng(rows * 31 + cols)
+    x = (rng.standard_normal((rows, cols)) * 2.0 ** rng.integers(-12, 12, (rows, 1))).astype(np.float32)
+    if dtype == torch.bfloat16:
+        x = workloads.to_bf16_values(x)
+    x = x.astype(np.float64)
+    rc, rs = mxfp4.quantize(x)
+    announce("quantize tiled guards", rows, cols, dtype)
+    cb = (rows + 1) // 2 * 2 * (cols // 2)
+    sb = (rows + 31) // 32 * 32 * (cols // 32)
+    g = 256
+    cbuf = torch.full((cb + 2 * g,), 0xA5, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((sb + 2 * g,), 0xA5, dtype=torch.uint8, device="cuda")
+    xd = dev(x, dtype)
+    st = ops.lib().fp4dit_quantize_mxfp4(xd.data_ptr(), ops.F32 if dtype == torch.float32 else ops.BF16, rows, cols,
+                                         cbuf.data_ptr() + g, sbuf.data_ptr() + g, ops.TILED,
+                                         torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    c, s_ = host(cbuf), host(sbuf)
+    parity.assert_codes_exact(layout.untile_codes(c[g:g + cb], rows, cols),
+                              layout.untile_scales(s_[g:g + sb], rows, cols), rc, rs, "tiled %dx%d" % (rows, cols))
+    assert (c[:g] == 0xA5).all() and (c[g + cb:] == 0xA5).all(), "bytes outside the codes"
+    assert (s_[:g] == 0xA5).all() and (s_[g + sb:] == 0xA5).all(), "bytes outside the scales"
