@@ -216,7 +216,11 @@ int32_t fp4dit_swiglu_interleave_group(void);
  * pointer 4-byte aligned.  Requires K % 128 == 0 and K >= 256 (the
  * 128-deep K stage, and the two stages the LDS ring's prologue loads),
  * N % 256 == 0 and N > 0, and M*K/2 and N*K/2 below 2^31 bytes; M >= 0 is
- * otherwise arbitrary (a ragged last token tile is masked).
+ * otherwise arbitrary (a ragged last token tile is masked).  The order of
+ * the fp32 sums follows the launch's grid, which is derived from the
+ * device's compute-unit count: on one device the same inputs give the same
+ * bits on every call; devices with other CU counts may differ in the last
+ * bits.
  */
 
 /*
